@@ -1,0 +1,225 @@
+#!/usr/bin/env python3
+"""Benchmark of the hot path on one MI355X; prints ONE JSON line on stdout.
+
+One step = one causal prefill forward (B=4, H=32, N=8192, d=128, bf16 in,
+fp32 accumulate, bf16 O + fp32 LSE) followed by one split-KV paged decode
+(64 sequences, 32 query / 8 KV heads, d=128, 16-token pages, lengths uniform
+in [1024, 32768], automatic split count) including its merge of partials.
+Inputs are seeded synthetic tensors, resident in HBM before timing starts.
+
+`value` is the prefill throughput in TFLOP/s of algorithmic work
+(4 d per visible query-key pair); the decode's KV GB/s is reported beside it.
+Both parts are timed with HIP events on the stream the kernels run on.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 4096 dense bf16 FLOP/clk x 2.4 GHz
+HBM_PEAK_GBPS = 8000.0
+PREFILL = "causal_prefill_bf16_b4_h32_n8192"
+DECODE = "paged_decode_bf16_b64_h32_kv8"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def causal_flops(B, H, N, d):
+    return 4.0 * d * (N * (N + 1) / 2) * B * H
+
+
+def cpu_baseline_prefill(q, k, v, d, target_s):
+    """Time the float64 oracle on whole heads' worth of evenly spaced rows."""
+    import numpy as np
+    import oracle
+    N = q.shape[1]
+    rows = np.arange(N // 256 - 1, N, N // 256)            # 256 rows spread over the sequence
+    per_head = sum(4.0 * d * (i + 1) for i in rows)
+    done, heads = 0.0, 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < target_s and heads < q.shape[0] * q.shape[2]:
+        b, h = divmod(heads, q.shape[2])
+        oracle.attention(q[b:b + 1, :, h:h + 1], k[b:b + 1, :, h:h + 1], v[b:b + 1, :, h:h + 1],
+                         1 / math.sqrt(d), True, rows=rows, block_rows=16)
+        done += per_head
+        heads += 1
+    dt = time.perf_counter() - t0
+    return dict(value=done / dt / 1e12, unit="TFLOP/s", cores=oracle.default_threads(),
+                kind="oracle",
+                sample=f"{heads} heads x 256 evenly spaced causal query rows of the "
+                       f"{PREFILL} workload, float64, {dt:.1f} s")
+
+
+def cpu_baseline_decode(pi, d, target_s):
+    import oracle
+    hkv = pi.k_pool.shape[2]
+    done_bytes, seqs = 0.0, 0
+    t0 = time.perf_counter()
+    B = pi.q.shape[0]
+    while time.perf_counter() - t0 < target_s and seqs < B:
+        b = seqs
+        oracle.decode_paged(pi.q[b:b + 1], pi.k_pool, pi.v_pool, pi.block_table[b:b + 1],
+                            pi.seq_lens[b:b + 1], 1 / math.sqrt(d))
+        done_bytes += float(pi.seq_lens[b]) * hkv * d * 2 * 2
+        seqs += 1
+    dt = time.perf_counter() - t0
+    return dict(value=done_bytes / dt / 1e9, unit="GB/s", cores=oracle.default_threads(),
+                kind="oracle",
+                sample=f"{seqs} of the {B} sequences of the {DECODE} workload, float64, "
+                       f"{dt:.1f} s")
+
+
+def copy_calibration(torch, nbytes=1 << 30, reps=5):
+    """A plain device copy of known size, for scaling HBM byte counters."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": nbytes, "bytes_written": nbytes,
+                      "dispatches": reps}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--parts", default="prefill,decode",
+                    help="comma list of the step's parts to run (profiling aid)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of each oracle baseline sample (0 = skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (for HBM counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build measures one GPU only; the library has no multi-GPU "
+              "path, so --gpus must be 1 (the per-GPU share is the whole workload).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import exact_tiled_attention_11_amd as fa
+    from exact_tiled_attention_11_amd import inputs
+
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
+
+    parts = set(args.parts.split(","))
+    dev = "cuda"
+    pp = inputs.WORKLOADS[PREFILL].params
+    dp = inputs.WORKLOADS[DECODE].params
+    B, H, N, d = pp["B"], pp["H"], pp["N"], pp["d"]
+
+    log(f"bench: generating {PREFILL} inputs")
+    q, k, v = inputs.prefill_inputs(B, H, pp["Hkv"], N, N, d, torch.bfloat16, pp["seed"])
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    o = torch.empty_like(qd)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    flops = causal_flops(B, H, N, d)
+
+    log(f"bench: generating {DECODE} inputs")
+    lens = inputs.uniform_lengths(dp["B"], dp["len_lo"], dp["len_hi"], dp["seed"])
+    pi = inputs.paged_decode_inputs(dp["B"], dp["H"], dp["Hkv"], dp["d"], lens, dp["seed"],
+                                    pool_factor=dp["pool_factor"], max_pages=dp["len_hi"] // 16)
+    dq, dk, dv = pi.q.to(dev), pi.k_pool.to(dev), pi.v_pool.to(dev)
+    dt_, ds_ = pi.block_table.to(dev), pi.seq_lens.to(dev)
+    od = torch.empty_like(dq)
+    lsed = torch.empty((dp["B"], dp["H"]), dtype=torch.float32, device=dev)
+    ws = torch.empty(fa.decode_workspace_size(dp["B"], dp["H"], dp["d"], fa.MAX_SPLITS),
+                     dtype=torch.uint8, device=dev)
+    kv_bytes = float(lens.sum()) * dp["Hkv"] * dp["d"] * 2 * 2
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        if "prefill" in parts:
+            fa.forward(qd, kd, vd, causal=True, out=o, lse=lse)
+        if ev is not None:
+            ev[1].record()
+        if "decode" in parts:
+            fa.decode_paged(dq, dk, dv, dt_, ds_, out=od, lse=lsed, workspace=ws)
+        if ev is not None:
+            ev[2].record()
+
+    log(f"bench: warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    log(f"bench: timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pre_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    dec_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    log(f"bench: prefill ms mean {pre_ms.mean():.3f} min {pre_ms.min():.3f}; "
+        f"decode ms mean {dec_ms.mean():.3f} min {dec_ms.min():.3f}")
+
+    pre_tflops = flops / (pre_ms.mean() * 1e-3) / 1e12 if "prefill" in parts else None
+    dec_gbps = kv_bytes / (dec_ms.mean() * 1e-3) / 1e9 if "decode" in parts else None
+
+    cpu = None
+    cpu_dec = None
+    if args.cpu_seconds > 0:
+        log("bench: timing the CPU oracle baseline")
+        cpu = cpu_baseline_prefill(q, k, v, d, args.cpu_seconds)
+        cpu_dec = cpu_baseline_decode(pi, d, args.cpu_seconds / 2)
+
+    line = {
+        "metric": "prefill attn TFLOP/s (% MFMA peak); split-KV decode KV GB/s (% HBM peak)",
+        "value": pre_tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": PREFILL + " + " + DECODE, "prefill": {k_: pp[k_] for k_ in
+                   ("B", "H", "Hkv", "N", "d")} | {"causal": True},
+                   "decode": {k_: dp[k_] for k_ in ("B", "H", "Hkv", "d", "page", "len_lo",
+                                                      "len_hi")} | {"splits": "auto"}},
+        "roofline": None if pre_tflops is None else {
+            "bound": "mfma", "achieved": pre_tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": pre_tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+            "kernel": "fwd_kernel<Policy16<BF16,128>,bf16,128,causal>",
+            "ms_mean": float(pre_ms.mean()), "ms_min": float(pre_ms.min()),
+            "algorithmic_flop_per_launch": flops},
+        "decode": None if dec_gbps is None else {
+            "value": dec_gbps, "unit": "GB/s", "bound": "hbm", "peak": HBM_PEAK_GBPS,
+            "frac": dec_gbps / HBM_PEAK_GBPS, "ms_mean": float(dec_ms.mean()),
+            "ms_min": float(dec_ms.min()), "kv_bytes": kv_bytes,
+            "timed": "decode kernel + merge kernel", "traffic": None},
+        "cpu_baseline": cpu,
+        "cpu_baseline_decode": cpu_dec,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

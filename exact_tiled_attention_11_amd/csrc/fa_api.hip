@@ -1,0 +1,135 @@
+// The extern "C" entry points of include/fa.h: argument validation on the
+// host, then launches on the caller's stream. Nothing here allocates or keeps
+// state; every check runs before the first HIP call so an invalid call has
+// no side effect at all.
+#include <cmath>
+#include <cstdint>
+
+#include "fa.h"
+#include "fa_internal.hpp"
+#include "fa_split_rule.hpp"
+
+namespace {
+
+constexpr int64_t kMaxElems = (int64_t{1} << 31) - 1;
+
+bool valid_dtype(fa_dtype t) { return t == FA_F32 || t == FA_F16 || t == FA_BF16; }
+bool head_dim_ok(int d) { return d == 64 || d == 128; }
+bool scale_ok(float s) { return std::isfinite(s) && s > 0.f; }
+
+fa_status from_hip(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+// The kernels move data in 16-byte vectors.
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_string(fa_status s) {
+  switch (s) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_NULL_PTR: return "FA_ERR_NULL_PTR: a required pointer is NULL";
+    case FA_ERR_BAD_SHAPE: return "FA_ERR_BAD_SHAPE: a size is negative, inconsistent or too large";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: valid but not implemented for these sizes or types";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or smaller than required";
+    case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported a launch failure";
+    case FA_ERR_BAD_ARG: return "FA_ERR_BAD_ARG: an argument is out of range";
+  }
+  return "unknown fa_status";
+}
+
+const char* fa_version(void) { return "0.1.0"; }
+
+fa_status fa_forward(const void* Q, const void* K, const void* V, void* O, float* LSE, int B,
+                     int H, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                     fa_dtype in_dtype, fa_dtype out_dtype, void* stream) {
+  if (B < 0 || Nq < 0 || Nk < 0 || H < 1 || Hkv < 1 || H % Hkv != 0) return FA_ERR_BAD_SHAPE;
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return FA_ERR_BAD_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_BAD_ARG;
+  if (!scale_ok(scale)) return FA_ERR_BAD_ARG;
+  if (!head_dim_ok(d)) return FA_ERR_UNSUPPORTED;
+  if (out_dtype != in_dtype && out_dtype != FA_F32) return FA_ERR_UNSUPPORTED;
+  const int64_t q_elems = int64_t{B} * Nq * H * d;
+  const int64_t kv_elems = int64_t{B} * Nk * Hkv * d;
+  const int64_t n_qblocks = (int64_t{Nq} + 127) / 128;
+  if (q_elems > kMaxElems || kv_elems > kMaxElems || int64_t{B} * H * n_qblocks > kMaxElems)
+    return FA_ERR_BAD_SHAPE;
+  if (B == 0 || Nq == 0) return FA_OK;
+  if (!Q || !O || !LSE || (Nk > 0 && (!K || !V))) return FA_ERR_NULL_PTR;
+  if (!aligned16(Q) || !aligned16(O) || (Nk > 0 && (!aligned16(K) || !aligned16(V))))
+    return FA_ERR_BAD_ARG;
+  fa::ForwardArgs a{Q, K, V, O, LSE, B, H, Hkv, Nq, Nk, d, scale, causal, in_dtype, out_dtype};
+  return from_hip(fa::launch_forward(a, static_cast<hipStream_t>(stream)));
+}
+
+int fa_decode_num_splits(int seq_len, int num_splits) {
+  if (seq_len < 0 || num_splits < 0 || num_splits > FA_MAX_SPLITS) return -1;
+  return fa::decode_splits(seq_len, num_splits);
+}
+
+size_t fa_decode_workspace_size(int B, int H, int d, int max_splits) {
+  if (B < 0 || H < 1 || d < 1 || max_splits < 1 || max_splits > FA_MAX_SPLITS) return 0;
+  const size_t rows = static_cast<size_t>(B) * static_cast<size_t>(H) * max_splits;
+  const size_t o_bytes = (rows * static_cast<size_t>(d) * sizeof(float) + 255) / 256 * 256;
+  return o_bytes + rows * sizeof(float);
+}
+
+fa_status fa_decode_paged(const void* q, const void* K_pool, const void* V_pool,
+                          const int32_t* block_table, const int32_t* seq_lens, void* O, float* LSE,
+                          int B, int H, int Hkv, int d, int page_size, int max_pages_per_seq,
+                          int num_pages, float scale, int num_splits, fa_dtype dtype,
+                          fa_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  if (B < 0 || H < 1 || Hkv < 1 || H % Hkv != 0 || max_pages_per_seq < 1 || num_pages < 1 ||
+      page_size < 1)
+    return FA_ERR_BAD_SHAPE;
+  if (num_splits < 0 || num_splits > FA_MAX_SPLITS) return FA_ERR_BAD_ARG;
+  if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return FA_ERR_BAD_ARG;
+  if (!scale_ok(scale)) return FA_ERR_BAD_ARG;
+  const int G = H / Hkv;
+  if (!head_dim_ok(d) || page_size != FA_PAGE_SIZE || dtype == FA_F32 ||
+      !(G == 1 || G == 2 || G == 4 || G == 8))
+    return FA_ERR_UNSUPPORTED;
+  if (out_dtype != dtype && out_dtype != FA_F32) return FA_ERR_UNSUPPORTED;
+  if (int64_t{num_pages} * page_size * Hkv * d > kMaxElems ||
+      int64_t{B} * max_pages_per_seq > kMaxElems || int64_t{B} * H * d > kMaxElems ||
+      int64_t{max_pages_per_seq} * page_size > kMaxElems || B > 65535 || Hkv > 65535)
+    return FA_ERR_BAD_SHAPE;
+  if (B == 0) return FA_OK;
+  if (!q || !K_pool || !V_pool || !block_table || !seq_lens || !O || !LSE)
+    return FA_ERR_NULL_PTR;
+  if (!aligned16(q) || !aligned16(K_pool) || !aligned16(V_pool)) return FA_ERR_BAD_ARG;
+  const int S = num_splits > 0 ? num_splits : FA_MAX_SPLITS;
+  const size_t need = fa_decode_workspace_size(B, H, d, S);
+  if (S > 1 && (workspace == nullptr || workspace_bytes < need)) return FA_ERR_WORKSPACE;
+  fa::DecodeArgs a;
+  a.q = q; a.k_pool = K_pool; a.v_pool = V_pool;
+  a.block_table = block_table; a.seq_lens = seq_lens;
+  a.o = O; a.lse = LSE;
+  a.B = B; a.H = H; a.Hkv = Hkv; a.d = d; a.page_size = page_size;
+  a.max_pages = max_pages_per_seq; a.num_pages = num_pages;
+  a.scale = scale; a.num_splits = num_splits;
+  a.dtype = dtype; a.out_dtype = out_dtype;
+  a.max_splits = S;
+  const size_t rows = static_cast<size_t>(B) * H * S;
+  a.part_o = static_cast<float*>(workspace);
+  a.part_lse = workspace ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                                    (rows * d * sizeof(float) + 255) / 256 * 256)
+                         : nullptr;
+  return from_hip(fa::launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+fa_status fa_merge_partials(const float* o_parts, const float* lse_parts, const int32_t* num_parts,
+                            void* O, float* LSE, int R, int S, int d, fa_dtype out_dtype,
+                            void* stream) {
+  if (R < 0 || S < 1 || S > 1024 || d < 1 || d > 1024) return FA_ERR_BAD_SHAPE;
+  if (!valid_dtype(out_dtype)) return FA_ERR_BAD_ARG;
+  if (int64_t{R} * S * d > kMaxElems) return FA_ERR_BAD_SHAPE;
+  if (R == 0) return FA_OK;
+  if (!o_parts || !lse_parts || !O || !LSE) return FA_ERR_NULL_PTR;
+  fa::MergeArgs a{o_parts, lse_parts, num_parts, O, LSE, R, S, d, out_dtype};
+  return from_hip(fa::launch_merge(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,131 @@
+// Device-side helpers shared by the gfx950 attention kernels: vector types,
+// matrix-core wrappers, cross-lane reductions and type conversions.
+//
+// Matrix-core operand layouts used throughout (wave64, verified on gfx950):
+//   32x32x16 (bf16/f16): lane l holds A[l%32][8*(l/32)+j] and B[8*(l/32)+j][l%32]
+//                        (j = 0..7); result register i of lane l is
+//                        C[8*(i/4) + 4*(l/32) + i%4][l%32].
+//   32x32x2 (f32):       lane l holds A[l%32][l/32] and B[l/32][l%32]; same C.
+//   16x16x32 (bf16/f16): lane l holds A[l%16][8*(l/16)+j], B[8*(l/16)+j][l%16];
+//                        result register i of lane l is C[4*(l/16)+i][l%16].
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.69314718055994531f;
+constexpr float kNegInf = -__builtin_inff();
+
+// 2^x on the transcendental unit (v_exp_f32); 2^-inf = 0.
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Reductions across the two halves of a wave (lane l and lane l^32). Both
+// lanes of a pair combine the operands in the same order, so they end up
+// with bitwise identical values.
+__device__ __forceinline__ float max_xor32(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// Reductions between 16-lane rows r and r^1 (lane l and lane l^16).
+__device__ __forceinline__ float max_xor16(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Element types. Storage is handled as raw 16-bit words; arithmetic types
+// are the compiler's __bf16 / _Float16.
+struct BF16 {
+  using scalar = __bf16;
+  using vec8 = bf16x8;
+  static __device__ __forceinline__ f32x16 mma32(vec8 a, vec8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mma16(vec8 a, vec8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ float to_f32(uint16_t u) {
+    return __uint_as_float(static_cast<uint32_t>(u) << 16);
+  }
+};
+struct F16 {
+  using scalar = _Float16;
+  using vec8 = f16x8;
+  static __device__ __forceinline__ f32x16 mma32(vec8 a, vec8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mma16(vec8 a, vec8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ float to_f32(uint16_t u) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, u));
+  }
+};
+
+// Round-to-nearest-even conversion of 8 floats into one matrix-core operand.
+template <typename E>
+__device__ __forceinline__ typename E::vec8 pack8(float a0, float a1, float a2, float a3,
+                                                  float a4, float a5, float a6, float a7) {
+  typename E::vec8 r;
+  r[0] = static_cast<typename E::scalar>(a0);
+  r[1] = static_cast<typename E::scalar>(a1);
+  r[2] = static_cast<typename E::scalar>(a2);
+  r[3] = static_cast<typename E::scalar>(a3);
+  r[4] = static_cast<typename E::scalar>(a4);
+  r[5] = static_cast<typename E::scalar>(a5);
+  r[6] = static_cast<typename E::scalar>(a6);
+  r[7] = static_cast<typename E::scalar>(a7);
+  return r;
+}
+
+// Output stores of 4 consecutive floats in the output element type.
+__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+}
+__device__ __forceinline__ void store4(__bf16* p, float a, float b, float c, float d) {
+  typedef __bf16 v4 __attribute__((ext_vector_type(4)));
+  v4 r;
+  r[0] = static_cast<__bf16>(a); r[1] = static_cast<__bf16>(b);
+  r[2] = static_cast<__bf16>(c); r[3] = static_cast<__bf16>(d);
+  *reinterpret_cast<v4*>(p) = r;
+}
+__device__ __forceinline__ void store4(_Float16* p, float a, float b, float c, float d) {
+  typedef _Float16 v4 __attribute__((ext_vector_type(4)));
+  v4 r;
+  r[0] = static_cast<_Float16>(a); r[1] = static_cast<_Float16>(b);
+  r[2] = static_cast<_Float16>(c); r[3] = static_cast<_Float16>(d);
+  *reinterpret_cast<v4*>(p) = r;
+}
+__device__ __forceinline__ void store1(float* p, float a) { *p = a; }
+__device__ __forceinline__ void store1(__bf16* p, float a) { *p = static_cast<__bf16>(a); }
+__device__ __forceinline__ void store1(_Float16* p, float a) { *p = static_cast<_Float16>(a); }
+
+// Workgroup id remap so that consecutive logical ids run on the same XCD.
+// The dispatcher hands workgroup p to XCD p % kXcds; here logical id L is
+// given to physical id p such that each XCD receives one contiguous range of
+// logical ids (their K/V then share that XCD's L2).
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_remap(int p, int total) {
+  const int q = total / kXcds, r = total % kXcds;
+  const int x = p % kXcds, k = p / kXcds;
+  const int base = (x < r) ? x * (q + 1) : r * (q + 1) + (x - r) * q;
+  return base + k;
+}
+
+}  // namespace fa

@@ -1,0 +1,415 @@
+// Tiled attention forward for gfx950: online softmax over key tiles held in
+// LDS, scores and the P V product on the matrix cores, causal tile skipping.
+//
+// The method is the one of "3.4 Attention Kernels", section "FlashAttention:
+// tiling" (also "FlashAttention and Optimized Kernels", section "The online
+// softmax"): for a block of query rows keep a running max m, running sum l and
+// unnormalised output acc; for each key tile compute the score tile, raise m,
+// rescale l and acc by e^(m_old - m_new), add the tile's contribution; write
+// O = acc / l and LSE = m + ln l once at the end (normalising once, as
+// section "FlashAttention-2 and -3" describes). Key tiles wholly above the
+// causal diagonal are never loaded.
+//
+// Work decomposition (one workgroup = 4 waves = 128 query rows of one
+// (batch, head); one key tile = 64 keys):
+//   * Each wave owns 32 query rows. Scores are computed transposed,
+//     S^T = K Q^T, so that every lane owns ONE query row (l % 32) and 32 of
+//     the tile's keys: the row max and row sum are in-lane reductions plus
+//     one exchange with lane l ^ 32, and the per-row rescale factor is a
+//     lane-local scalar.
+//   * The score accumulator, after exponentiation and rounding to the input
+//     type, is directly the B operand of O^T += V^T P^T: no LDS round trip.
+//     The contraction over keys uses the keys in the order the score layout
+//     delivers them; V^T is fetched in that same key order.
+//   * K and V tiles are staged in LDS, double buffered: the global loads of
+//     tile j+1 are in flight while tile j is computed. V stays row-major in
+//     LDS; the transposed operand comes from ds_read_b64_tr_b16.
+//   * Softmax runs in base 2 with scale*log2(e) folded into one FMA; m is
+//     kept in raw-score units so LSE comes back in natural-log units.
+#include "fa_device.hpp"
+#include "fa_internal.hpp"
+
+namespace fa {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kQPW = 32;              // query rows per wave
+constexpr int kBR = kWaves * kQPW;    // query rows per workgroup
+constexpr int kBC = 64;               // keys per tile
+
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, H, Hkv, Nq, Nk;
+  int group;       // H / Hkv
+  int n_qblocks;   // ceil(Nq / kBR)
+  int total;       // B * H * n_qblocks
+  float c;         // scale * log2(e)
+  int off;         // Nk - Nq: key j is visible to query i iff j <= i + off
+};
+
+// ---------------------------------------------------------------------------
+// bf16 / fp16 inputs: 32x32x16 matrix-core ops.
+// ---------------------------------------------------------------------------
+template <class E, int D>
+struct Policy16 {
+  using In = uint16_t;
+  static constexpr int KS = D + 8;     // K row stride in LDS (elements): conflict-free 16B reads
+  static constexpr int VS = D + 16;    // V row stride: conflict-free transposed reads
+  static constexpr int K_ELEMS = kBC * KS;
+  static constexpr int V_ELEMS = kBC * VS;
+  static constexpr int BUF_BYTES = (K_ELEMS + V_ELEMS) * 2;
+  static constexpr int CPR = D / 8;    // 16-byte chunks per row
+  static constexpr int PER_THREAD = kBC * CPR / kThreads;
+  static constexpr int QF = D / 16;
+  static_assert(PER_THREAD * kThreads == kBC * CPR, "tile must split evenly");
+
+  typename E::vec8 qf[QF];     // B operand of S^T = K Q^T
+  uint4 kst[PER_THREAD];
+  uint4 vst[PER_THREAD];
+
+  // Lane l holds Q[row][16c + 8(l/32) .. +8] for c = 0..D/16-1.
+  __device__ __forceinline__ void load_q(const In* qrow, bool valid, int lane) {
+    const int base = 8 * (lane >> 5);
+#pragma unroll
+    for (int c = 0; c < QF; ++c) {
+      uint4 u = make_uint4(0, 0, 0, 0);
+      if (valid) u = *reinterpret_cast<const uint4*>(qrow + 16 * c + base);
+      qf[c] = __builtin_bit_cast(typename E::vec8, u);
+    }
+  }
+
+  __device__ __forceinline__ void stage_load(const In* kb, const In* vb, int64_t rs, int k0,
+                                             int nk, int tid) {
+#pragma unroll
+    for (int r = 0; r < PER_THREAD; ++r) {
+      const int ci = tid + r * kThreads;
+      const int key = k0 + ci / CPR, dc = ci % CPR;
+      uint4 ku = make_uint4(0, 0, 0, 0), vu = make_uint4(0, 0, 0, 0);
+      if (key < nk) {
+        ku = *reinterpret_cast<const uint4*>(kb + key * rs + dc * 8);
+        vu = *reinterpret_cast<const uint4*>(vb + key * rs + dc * 8);
+      }
+      kst[r] = ku;
+      vst[r] = vu;
+    }
+  }
+
+  __device__ __forceinline__ void stage_store(unsigned char* buf, int tid) {
+    In* kl = reinterpret_cast<In*>(buf);
+    In* vl = kl + K_ELEMS;
+#pragma unroll
+    for (int r = 0; r < PER_THREAD; ++r) {
+      const int ci = tid + r * kThreads;
+      const int key = ci / CPR, dc = ci % CPR;
+      *reinterpret_cast<uint4*>(kl + key * KS + dc * 8) = kst[r];
+      *reinterpret_cast<uint4*>(vl + key * VS + dc * 8) = vst[r];
+    }
+  }
+
+  // s[kb] = S^T rows 32kb..32kb+31 (keys) x 32 query rows of this wave.
+  __device__ __forceinline__ void scores(const unsigned char* buf, int lane, f32x16 s[2]) const {
+    const In* kl = reinterpret_cast<const In*>(buf);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 acc = {};
+      const In* row = kl + (32 * kb + (lane & 31)) * KS + 8 * (lane >> 5);
+#pragma unroll
+      for (int c = 0; c < QF; ++c) {
+        const auto a = *reinterpret_cast<const typename E::vec8*>(row + 16 * c);
+        acc = E::mma32(a, qf[c], acc);
+      }
+      s[kb] = acc;
+    }
+  }
+
+  // acc[db] += V^T[32db.., keys] P^T[keys, rows]. Register i of p[kb] holds
+  // key 32kb + 8(i/4) + 4(l/32) + i%4; the P V contraction takes them 8 at a
+  // time (registers 8hh..8hh+7) and fetches V^T for exactly those keys with
+  // two transposed LDS reads.
+  __device__ __forceinline__ void pv(const unsigned char* buf, int lane, const f32x16 p[2],
+                                     f32x16* acc) const {
+    const In* vl = reinterpret_cast<const In*>(buf) + K_ELEMS;
+    const int blk = lane >> 4, r = lane & 15;
+    const int dlane = 16 * (blk & 1) + 4 * (r & 3);
+    const int klane = 4 * (blk >> 1) + (r >> 2);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int o = 8 * hh;
+        const auto bop = pack8<E>(p[kb][o + 0], p[kb][o + 1], p[kb][o + 2], p[kb][o + 3],
+                                  p[kb][o + 4], p[kb][o + 5], p[kb][o + 6], p[kb][o + 7]);
+        const In* rowp = vl + (32 * kb + 16 * hh + klane) * VS + dlane;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const In* a0 = rowp + 32 * db;
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(a0));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(a0 + 8 * VS));
+          typedef short i16x8 __attribute__((ext_vector_type(8)));
+          const i16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          acc[db] = E::mma32(__builtin_bit_cast(typename E::vec8, w), bop, acc[db]);
+        }
+      }
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// fp32 inputs: 32x32x2 fp32 matrix-core ops, probabilities kept in fp32.
+// ---------------------------------------------------------------------------
+template <int D>
+struct PolicyF32 {
+  using In = float;
+  static constexpr int KS = D + 1;     // odd stride: column reads hit 32 distinct banks
+  static constexpr int VS = D + 4;
+  static constexpr int K_ELEMS = kBC * KS;
+  static constexpr int V_ELEMS = kBC * VS;
+  static constexpr int BUF_BYTES = (K_ELEMS + V_ELEMS) * 4;
+  static constexpr int CPR = D / 4;
+  static constexpr int PER_THREAD = kBC * CPR / kThreads;
+  static constexpr int QF = D / 2;
+  static_assert(PER_THREAD * kThreads == kBC * CPR, "tile must split evenly");
+
+  float qf[QF];   // Q[row][c + (D/2)(l/32)]
+  float4 kst[PER_THREAD];
+  float4 vst[PER_THREAD];
+
+  __device__ __forceinline__ void load_q(const In* qrow, bool valid, int lane) {
+    const In* p = qrow + (D / 2) * (lane >> 5);
+#pragma unroll
+    for (int c = 0; c < QF; c += 4) {
+      float4 u = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (valid) u = *reinterpret_cast<const float4*>(p + c);
+      qf[c] = u.x; qf[c + 1] = u.y; qf[c + 2] = u.z; qf[c + 3] = u.w;
+    }
+  }
+
+  __device__ __forceinline__ void stage_load(const In* kb, const In* vb, int64_t rs, int k0,
+                                             int nk, int tid) {
+#pragma unroll
+    for (int r = 0; r < PER_THREAD; ++r) {
+      const int ci = tid + r * kThreads;
+      const int key = k0 + ci / CPR, dc = ci % CPR;
+      float4 ku = make_float4(0.f, 0.f, 0.f, 0.f), vu = ku;
+      if (key < nk) {
+        ku = *reinterpret_cast<const float4*>(kb + key * rs + dc * 4);
+        vu = *reinterpret_cast<const float4*>(vb + key * rs + dc * 4);
+      }
+      kst[r] = ku;
+      vst[r] = vu;
+    }
+  }
+
+  __device__ __forceinline__ void stage_store(unsigned char* buf, int tid) {
+    In* kl = reinterpret_cast<In*>(buf);
+    In* vl = kl + K_ELEMS;
+#pragma unroll
+    for (int r = 0; r < PER_THREAD; ++r) {
+      const int ci = tid + r * kThreads;
+      const int key = ci / CPR, dc = ci % CPR;
+      In* kp = kl + key * KS + dc * 4;
+      kp[0] = kst[r].x; kp[1] = kst[r].y; kp[2] = kst[r].z; kp[3] = kst[r].w;
+      *reinterpret_cast<float4*>(vl + key * VS + dc * 4) = vst[r];
+    }
+  }
+
+  __device__ __forceinline__ void scores(const unsigned char* buf, int lane, f32x16 s[2]) const {
+    const In* kl = reinterpret_cast<const In*>(buf);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 acc = {};
+      const In* row = kl + (32 * kb + (lane & 31)) * KS + (D / 2) * (lane >> 5);
+#pragma unroll
+      for (int c = 0; c < QF; ++c)
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(row[c], qf[c], acc, 0, 0, 0);
+      s[kb] = acc;
+    }
+  }
+
+  // Step (kb, i) contracts over the pair of keys held in register i by the
+  // two half-waves: key 32kb + 8(i/4) + i%4 (+4 for the upper half).
+  __device__ __forceinline__ void pv(const unsigned char* buf, int lane, const f32x16 p[2],
+                                     f32x16* acc) const {
+    const In* vl = reinterpret_cast<const In*>(buf) + K_ELEMS;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = 32 * kb + 8 * (i >> 2) + (i & 3) + 4 * (lane >> 5);
+        const In* vrow = vl + key * VS + (lane & 31);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vrow[32 * db], p[kb][i], acc[db], 0, 0, 0);
+      }
+    }
+  }
+};
+
+template <class P, typename OutT, int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) void fwd_kernel(const FwdParams a) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * P::BUF_BYTES];
+  using In = typename P::In;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  const int L = xcd_remap(static_cast<int>(blockIdx.x), a.total);
+  const int bh = L / a.n_qblocks;
+  int qb = L - bh * a.n_qblocks;
+  if (CAUSAL) qb = a.n_qblocks - 1 - qb;   // longest causal rows first within each head
+  const int b = bh / a.H, h = bh - b * a.H, hk = h / a.group;
+  const int q0 = qb * kBR;
+  const int qw0 = q0 + wave * kQPW;
+  const int qrow = qw0 + (lane & 31);
+
+  const int64_t q_rs = static_cast<int64_t>(a.H) * D;
+  const int64_t kv_rs = static_cast<int64_t>(a.Hkv) * D;
+  const In* kbase = static_cast<const In*>(a.k) + static_cast<int64_t>(b) * a.Nk * kv_rs +
+                    static_cast<int64_t>(hk) * D;
+  const In* vbase = static_cast<const In*>(a.v) + static_cast<int64_t>(b) * a.Nk * kv_rs +
+                    static_cast<int64_t>(hk) * D;
+
+  P pol;
+  pol.load_q(static_cast<const In*>(a.q) + (static_cast<int64_t>(b) * a.Nq + qrow) * q_rs +
+                 static_cast<int64_t>(h) * D,
+             qrow < a.Nq, lane);
+
+  int last_key = a.Nk - 1;
+  int wave_last = a.Nk - 1;
+  if (CAUSAL) {
+    last_key = min(last_key, q0 + kBR - 1 + a.off);
+    wave_last = min(wave_last, qw0 + kQPW - 1 + a.off);
+  }
+  const int n_tiles = last_key >= 0 ? last_key / kBC + 1 : 0;
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
+  float m_run = kNegInf, m2_run = kNegInf, l_run = 0.f;
+
+  if (n_tiles > 0) {
+    pol.stage_load(kbase, vbase, kv_rs, 0, a.Nk, tid);
+    pol.stage_store(smem, tid);
+  }
+  __syncthreads();
+
+  for (int j = 0; j < n_tiles; ++j) {
+    const int k0 = j * kBC;
+    if (j + 1 < n_tiles) pol.stage_load(kbase, vbase, kv_rs, k0 + kBC, a.Nk, tid);
+    if (k0 <= wave_last) {
+      const unsigned char* buf = smem + (j & 1) * P::BUF_BYTES;
+      f32x16 s[2];
+      pol.scores(buf, lane, s);
+
+      const bool need_mask = (k0 + kBC > a.Nk) || (CAUSAL && k0 + kBC - 1 > qw0 + a.off);
+      if (need_mask) {
+        const int lim = CAUSAL ? min(a.Nk - 1, qrow + a.off) : a.Nk - 1;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = k0 + 32 * kb + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+            if (key > lim) s[kb][i] = kNegInf;
+          }
+      }
+
+      // Online softmax update for this lane's query row.
+      float mx = kNegInf;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+      mx = max_xor32(mx);
+      const float m_new = fmaxf(m_run, mx);
+      const float m2_new = m_new * a.c;
+      const float m2_use = (m_new == kNegInf) ? 0.f : m2_new;
+      const float alpha = (m_new == m_run) ? 1.f : exp2_fast(m2_run - m2_new);
+      float rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = exp2_fast(fmaf(s[kb][i], a.c, -m2_use));
+          s[kb][i] = p;
+          rs += p;
+        }
+      l_run = fmaf(alpha, l_run, rs);
+      if (__any(alpha != 1.f)) {
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+      }
+      m_run = m_new;
+      m2_run = m2_new;
+
+      pol.pv(buf, lane, s, acc);
+    }
+    if (j + 1 < n_tiles) pol.stage_store(smem + ((j + 1) & 1) * P::BUF_BYTES, tid);
+    __syncthreads();
+  }
+
+  // Epilogue: normalise once, store O in the output type and LSE in fp32.
+  const float l_tot = sum_xor32(l_run);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (qrow < a.Nq) {
+    OutT* orow = static_cast<OutT*>(a.o) + (static_cast<int64_t>(b) * a.Nq + qrow) * q_rs +
+                 static_cast<int64_t>(h) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        store4(orow + 32 * db + 8 * g + 4 * (lane >> 5), acc[db][4 * g] * inv,
+               acc[db][4 * g + 1] * inv, acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv);
+    if (lane < 32)
+      a.lse[(static_cast<int64_t>(b) * a.H + h) * a.Nq + qrow] =
+          l_tot > 0.f ? (m2_run + log2f(l_tot)) * kLn2 : kNegInf;
+  }
+}
+
+template <class P, typename OutT, int D>
+hipError_t launch_t(const FwdParams& p, bool causal, hipStream_t s) {
+  if (causal)
+    hipLaunchKernelGGL((fwd_kernel<P, OutT, D, true>), dim3(p.total), dim3(kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL((fwd_kernel<P, OutT, D, false>), dim3(p.total), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t dispatch_d(const FwdParams& p, const ForwardArgs& a, hipStream_t s) {
+  const bool c = a.causal != 0;
+  switch (a.in_dtype) {
+    case FA_BF16:
+      return a.out_dtype == FA_F32 ? launch_t<Policy16<BF16, D>, float, D>(p, c, s)
+                                   : launch_t<Policy16<BF16, D>, __bf16, D>(p, c, s);
+    case FA_F16:
+      return a.out_dtype == FA_F32 ? launch_t<Policy16<F16, D>, float, D>(p, c, s)
+                                   : launch_t<Policy16<F16, D>, _Float16, D>(p, c, s);
+    case FA_F32:
+      return launch_t<PolicyF32<D>, float, D>(p, c, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_forward(const ForwardArgs& a, hipStream_t s) {
+  FwdParams p;
+  p.q = a.q; p.k = a.k; p.v = a.v; p.o = a.o; p.lse = a.lse;
+  p.B = a.B; p.H = a.H; p.Hkv = a.Hkv; p.Nq = a.Nq; p.Nk = a.Nk;
+  p.group = a.H / a.Hkv;
+  p.n_qblocks = (a.Nq + kBR - 1) / kBR;
+  p.total = a.B * a.H * p.n_qblocks;
+  p.c = a.scale * kLog2e;
+  p.off = a.Nk - a.Nq;
+  if (p.total == 0) return hipSuccess;
+  return a.d == 64 ? dispatch_d<64>(p, a, s) : dispatch_d<128>(p, a, s);
+}
+
+}  // namespace fa

@@ -1,0 +1,57 @@
+// Internal launch interfaces between the C ABI layer (fa_api.hip) and the
+// kernel translation units. Arguments reaching these functions have been
+// validated already.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "fa.h"
+
+namespace fa {
+
+struct ForwardArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, H, Hkv, Nq, Nk, d;
+  float scale;
+  int causal;
+  fa_dtype in_dtype, out_dtype;
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  void* o;
+  float* lse;
+  int B, H, Hkv, d, page_size, max_pages, num_pages;
+  float scale;
+  int num_splits;  // 0 = per-sequence rule, else fixed
+  fa_dtype dtype, out_dtype;
+  float* part_o;    // [B, H, S, d] fp32
+  float* part_lse;  // [B, H, S]    fp32
+  int max_splits;   // S
+};
+
+struct MergeArgs {
+  const float* o_parts;
+  const float* lse_parts;
+  const int32_t* num_parts;  // may be NULL
+  void* o;
+  float* lse;
+  int R, S, d;
+  fa_dtype out_dtype;
+};
+
+hipError_t launch_forward(const ForwardArgs& a, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
+
+}  // namespace fa

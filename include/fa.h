@@ -1,0 +1,198 @@
+/*
+ * fa.h - C ABI of an exact tiled attention library for AMD MI355X (gfx950).
+ *
+ * Three operations, each exact up to floating-point reordering:
+ *
+ *   fa_forward         tiled attention forward with an online softmax and
+ *                      causal tile skipping ("3.4 Attention Kernels",
+ *                      section "FlashAttention: tiling"; "FlashAttention and
+ *                      Optimized Kernels", section "The online softmax").
+ *   fa_decode_paged    one query token per sequence against a paged, ragged
+ *                      KV cache, the keys split into chunks whose partial
+ *                      results are merged ("3.4 Attention Kernels", sections
+ *                      "Decode attention and Flash-Decoding" and "Paged and
+ *                      ragged layouts: FlashInfer").
+ *   fa_merge_partials  the merge of partial results computed on disjoint key
+ *                      sets ("3.4 Attention Kernels", section "Online softmax",
+ *                      last paragraph).
+ *
+ * Conventions shared by every call
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller; the
+ *     library keeps no pointer after the call returns and allocates nothing.
+ *   - Tensors are dense and contiguous in the layouts stated per call. The
+ *     Q, K, V, O, q and K/V pool pointers must be 16-byte aligned (else
+ *     FA_ERR_BAD_ARG); the kernels move them in 16-byte vectors.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is enqueued asynchronously on it; outputs are valid once the
+ *     stream has been synchronised. The library holds no global mutable
+ *     state, so calls on different streams may run concurrently provided
+ *     their output buffers do not overlap.
+ *   - Every argument is validated on the host BEFORE anything is launched.
+ *     A call that returns an error status has enqueued no work and has not
+ *     touched any buffer. FA_ERR_HIP reports a failed launch
+ *     (hipGetLastError after the launch); no C++ exception crosses the ABI.
+ *   - Softmax scale is explicit. LSE is the natural-log log-sum-exp of the
+ *     scaled scores over the visible keys, m + ln(l) ("3.4 Attention
+ *     Kernels", section "FlashAttention: tiling"). A query with no visible
+ *     key gets O = 0 and LSE = -inf.
+ *   - Grouped-query heads: query head h reads KV head h / (H / Hkv).
+ */
+#ifndef FA_MI355X_H
+#define FA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL_PTR = 1,    /* a required pointer is NULL                     */
+  FA_ERR_BAD_SHAPE = 2,   /* a size is negative, inconsistent or too large  */
+  FA_ERR_UNSUPPORTED = 3, /* valid but not implemented (head dim, dtype...) */
+  FA_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than required        */
+  FA_ERR_HIP = 5,         /* the HIP runtime reported a launch failure      */
+  FA_ERR_BAD_ARG = 6      /* a non-size argument is out of range            */
+} fa_status;
+
+typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
+
+/* Largest number of key splits per sequence fa_decode_paged uses. */
+#define FA_MAX_SPLITS 16
+/* Token slots per KV page accepted by fa_decode_paged. */
+#define FA_PAGE_SIZE 16
+
+/*
+ * fa_forward - exact attention forward for dense batched tensors.
+ *
+ * For every batch b, query head h and query row i:
+ *   s_ij = scale * Q[b,i,h,:] . K[b,j,h/(H/Hkv),:]
+ *   O[b,i,h,:] = sum_j softmax_j(s_ij) V[b,j,h/(H/Hkv),:],  LSE[b,h,i] = ln sum_j e^s_ij
+ * over the visible keys j ("3.4 Attention Kernels", sections "Naive attention
+ * and its memory traffic" and "FlashAttention: tiling"). With causal != 0 key
+ * j is visible to query i iff j <= i + (Nk - Nq): the causal diagonal is
+ * aligned to the bottom-right corner, as in the page's naive_attention code,
+ * which equals the usual alignment when Nq == Nk. Key tiles that lie wholly
+ * above the diagonal are never read ("tiles entirely above the diagonal are
+ * skipped").
+ *
+ * Layouts (row-major, contiguous):
+ *   Q   [B, Nq, H,   d]  in_dtype
+ *   K,V [B, Nk, Hkv, d]  in_dtype
+ *   O   [B, Nq, H,   d]  out_dtype (in_dtype, or FA_F32)
+ *   LSE [B, H, Nq]       float
+ * Arithmetic: bf16/fp16 inputs multiply on the matrix cores with fp32
+ * accumulation; the probabilities are rounded to the input type for the P V
+ * product. fp32 inputs use fp32 throughout. Outputs are rounded to nearest
+ * even once, at the store.
+ *
+ * Supported: d in {64, 128}; in_dtype in {FA_F32, FA_F16, FA_BF16};
+ * out_dtype == in_dtype or FA_F32; B, Nq, Nk >= 0; H, Hkv >= 1, H % Hkv == 0;
+ * every tensor below 2^31 elements. B == 0 or Nq == 0 is a no-op. Nk == 0
+ * writes O = 0 and LSE = -inf. Q, O, LSE (and K, V when Nk > 0) must be
+ * non-NULL; scale must be finite.
+ */
+fa_status fa_forward(const void* Q, const void* K, const void* V, void* O,
+                     float* LSE, int B, int H, int Hkv, int Nq, int Nk, int d,
+                     float scale, int causal, fa_dtype in_dtype,
+                     fa_dtype out_dtype, void* stream);
+
+/*
+ * fa_decode_num_splits - the number of key chunks fa_decode_paged uses for a
+ * sequence of seq_len tokens. num_splits > 0 forces that count;
+ * num_splits == 0 picks ceil(seq_len / 2048) clamped to [1, FA_MAX_SPLITS],
+ * so long sequences spread over more workgroups while short ones avoid
+ * merge overhead ("3.4 Attention Kernels", "In practice": kernels choose the
+ * number of splits from the context length). Returns -1 for invalid input.
+ * Pure host function; the kernels evaluate the same rule on the device.
+ */
+int fa_decode_num_splits(int seq_len, int num_splits);
+
+/*
+ * fa_decode_workspace_size - bytes of device workspace fa_decode_paged needs
+ * for B sequences of H query heads of dimension d with up to max_splits
+ * chunks per sequence (use FA_MAX_SPLITS when num_splits == 0).
+ * The workspace holds one fp32 partial (o[d], lse) per (b, h, chunk).
+ * Returns 0 for invalid sizes.
+ */
+size_t fa_decode_workspace_size(int B, int H, int d, int max_splits);
+
+/*
+ * fa_decode_paged - one query token per sequence against a paged KV cache.
+ *
+ * Sequence b has seq_lens[b] cached tokens; token t lives in page
+ * block_table[b * max_pages_per_seq + t / page_size] at slot t % page_size
+ * ("3.4 Attention Kernels", "Paged and ragged layouts": the block table plus
+ * the length of the last page, given here as the sequence length). Table
+ * entries past the last used page are never read. The tokens are cut into
+ * fa_decode_num_splits(seq_lens[b], num_splits) near-equal, page-aligned
+ * chunks; each chunk's partial (o = acc / l, lse = m + ln l) is computed
+ * independently and the partials are merged by the merge rule
+ * ("Decode attention and Flash-Decoding"). All query heads that share a KV
+ * head are processed together so each loaded K/V row serves all of them
+ * (the GQA paragraph of the same section).
+ *
+ * Layouts (row-major, contiguous):
+ *   q            [B, H, d]                          dtype
+ *   K_pool,V_pool[num_pages, page_size, Hkv, d]     dtype
+ *   block_table  [B, max_pages_per_seq]  int32      device memory
+ *   seq_lens     [B]                     int32      device memory
+ *   O            [B, H, d]                          out_dtype (dtype or FA_F32)
+ *   LSE          [B, H]                  float
+ *   workspace    >= fa_decode_workspace_size(B, H, d, S) bytes, S = num_splits
+ *                or FA_MAX_SPLITS when num_splits == 0; device memory,
+ *                contents on entry are ignored, on exit unspecified.
+ *
+ * Supported: dtype in {FA_F16, FA_BF16}; d in {64, 128}; page_size ==
+ * FA_PAGE_SIZE; 0 <= num_splits <= FA_MAX_SPLITS; H % Hkv == 0 and
+ * H / Hkv in {1, 2, 4, 8}; B <= 65535. A sequence of length 0 gets O = 0,
+ * LSE = -inf.
+ * Device-side contract (not checkable on the host without a sync):
+ * 0 <= seq_lens[b] <= max_pages_per_seq * page_size and every used table
+ * entry lies in [0, num_pages). A sequence that breaks it is not read out of
+ * bounds: its O and LSE are set to NaN instead.
+ */
+fa_status fa_decode_paged(const void* q, const void* K_pool,
+                          const void* V_pool, const int32_t* block_table,
+                          const int32_t* seq_lens, void* O, float* LSE, int B,
+                          int H, int Hkv, int d, int page_size,
+                          int max_pages_per_seq, int num_pages, float scale,
+                          int num_splits, fa_dtype dtype, fa_dtype out_dtype,
+                          void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/*
+ * fa_merge_partials - merge partial results over disjoint key sets.
+ *
+ * For each row r the first n = num_parts[r] parts (all S when num_parts is
+ * NULL) are combined with a common reference M = max_c lse[r,c]:
+ *   w_c = e^(lse[r,c] - M),  O[r,:] = sum_c w_c o[r,c,:] / sum_c w_c,
+ *   LSE[r] = M + ln sum_c w_c
+ * ("3.4 Attention Kernels", section "Online softmax", the merge of (m, l, acc)
+ * triples; a stored partial (o, lse) is the triple (lse, 1, o)). Parts with
+ * lse = -inf are empty and contribute nothing; a row whose parts are all
+ * empty gets O = 0, LSE = -inf. The sum runs in a fixed order (no atomics),
+ * so repeated calls give bitwise identical results.
+ *
+ * Layouts: o_parts [R, S, d] float; lse_parts [R, S] float; num_parts [R]
+ * int32 (device memory, each in [0, S]) or NULL; O [R, d] out_dtype; LSE [R]
+ * float. Supported: R >= 0, 1 <= S <= 1024, 1 <= d <= 1024, any out_dtype.
+ */
+fa_status fa_merge_partials(const float* o_parts, const float* lse_parts,
+                            const int32_t* num_parts, void* O, float* LSE,
+                            int R, int S, int d, fa_dtype out_dtype,
+                            void* stream);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* fa_status_string(fa_status status);
+
+/* Library version as "major.minor.patch" (static storage). */
+const char* fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_H */

@@ -76,6 +76,10 @@ def default_threads() -> int:
 
 
 def _f64(x) -> np.ndarray:
+    """float64 copy of an array; torch CPU tensors (bf16/fp16 included) are
+    converted by torch itself, exactly, since numpy has no bfloat16."""
+    if type(x).__module__.startswith("torch"):
+        return x.detach().to("cpu").double().numpy()
     return np.asarray(x, dtype=np.float64)
 
 
