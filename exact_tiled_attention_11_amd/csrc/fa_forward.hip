@@ -53,113 +53,224 @@ struct FwdParams {
 };
 
 // ---------------------------------------------------------------------------
-// bf16 / fp16 inputs: 32x32x16 matrix-core ops.
+// bf16 / fp16 inputs: 32x32x16 matrix-core ops, K/V tiles loaded straight
+// into LDS (no register staging), 2 waves per SIMD.
 // ---------------------------------------------------------------------------
-template <class E, int D>
-struct Policy16 {
-  using In = uint16_t;
-  static constexpr int KS = D + 8;     // K row stride in LDS (elements): conflict-free 16B reads
-  static constexpr int VS = D + 16;    // V row stride: conflict-free transposed reads
-  static constexpr int K_ELEMS = kBC * KS;
-  static constexpr int V_ELEMS = kBC * VS;
-  static constexpr int BUF_BYTES = (K_ELEMS + V_ELEMS) * 2;
-  static constexpr int CPR = D / 8;    // 16-byte chunks per row
-  static constexpr int PER_THREAD = kBC * CPR / kThreads;
-  static constexpr int QF = D / 16;
-  static_assert(PER_THREAD * kThreads == kBC * CPR, "tile must split evenly");
 
-  typename E::vec8 qf[QF];     // B operand of S^T = K Q^T
-  uint4 kst[PER_THREAD];
-  uint4 vst[PER_THREAD];
+// LDS tiles are unpadded [kBC rows][D] with the 16-byte chunks of each row
+// permuted by an XOR with swz(row), so that both the K operand reads (16
+// lanes x 16 B per cycle, 16 consecutive rows) and the transposed V reads
+// (32 lanes x 8 B per cycle, 4 rows x 4 chunks) hit 64 distinct banks.
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (D == 128) {
+    return 4 * (row & 3) + ((row >> 2) & 3);
+  } else {
+    const int b = (row >> 1) & 7;
+    return ((b & 1) << 2) | (b & 2) | ((b >> 2) & 1);
+  }
+}
 
-  // Lane l holds Q[row][16c + 8(l/32) .. +8] for c = 0..D/16-1.
-  __device__ __forceinline__ void load_q(const In* qrow, bool valid, int lane) {
-    const int base = 8 * (lane >> 5);
+template <int D, int NW>
+__device__ __forceinline__ void load_kv_tile(const uint16_t* kbase, const uint16_t* vbase,
+                                             int64_t rs, int k0, int nk, uint16_t* kl,
+                                             uint16_t* vl, int wave, int lane) {
+  constexpr int CPR = D / 8;
+  constexpr int SLABS_PER_WAVE = kBC * CPR / 64 / NW;
+#pragma unroll
+  for (int r = 0; r < SLABS_PER_WAVE; ++r) {
+    const int slab = wave * SLABS_PER_WAVE + r;
+    const int slot = slab * 64 + lane;
+    const int row = slot / CPR;
+    const int chunk = (slot % CPR) ^ swz<D>(row);
+    const int64_t key = min(k0 + row, nk - 1);
+    const int64_t off = key * rs + chunk * 8;
+    __builtin_amdgcn_global_load_lds(kbase + off, kl + slab * 512, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vbase + off, vl + slab * 512, 16, 0, 0);
+  }
+}
+
+template <class E, typename OutT, int D, bool CAUSAL, int NW>
+__global__ __launch_bounds__(NW * 64, 8 / NW)
+void fwd16_kernel(const FwdParams a) {
+  constexpr int TILE = kBC * D;                 // elements per K or V tile
+  constexpr int CPR = D / 8;                    // 16-byte chunks per row
+  constexpr int SLABS = kBC * CPR / 64;         // 1 KiB wave-loads per tensor per tile
+  constexpr int SLABS_PER_WAVE = SLABS / NW;
+  constexpr int QF = D / 16;
+  constexpr int BR = NW * kQPW;
+  static_assert(SLABS_PER_WAVE * NW == SLABS, "tile must split evenly over the waves");
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2][2][TILE];   // [buffer][K, V]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int L = xcd_remap(static_cast<int>(blockIdx.x), a.total);
+  const int bh = L / a.n_qblocks;
+  int qb = L - bh * a.n_qblocks;
+  if (CAUSAL) qb = a.n_qblocks - 1 - qb;   // longest causal rows first within each head
+  const int b = bh / a.H, h = bh - b * a.H, hk = h / a.group;
+  const int q0 = qb * BR;
+  const int qw0 = q0 + wave * kQPW;
+  const int qrow = qw0 + (lane & 31);
+
+  const int64_t q_rs = static_cast<int64_t>(a.H) * D;
+  const int64_t kv_rs = static_cast<int64_t>(a.Hkv) * D;
+  const uint16_t* kbase = static_cast<const uint16_t*>(a.k) +
+                          static_cast<int64_t>(b) * a.Nk * kv_rs + static_cast<int64_t>(hk) * D;
+  const uint16_t* vbase = static_cast<const uint16_t*>(a.v) +
+                          static_cast<int64_t>(b) * a.Nk * kv_rs + static_cast<int64_t>(hk) * D;
+
+  // Q^T operand: lane l holds Q[row][16c + 8(l/32) .. +8].
+  typename E::vec8 qf[QF];
+  {
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
+                         (static_cast<int64_t>(b) * a.Nq + qrow) * q_rs +
+                         static_cast<int64_t>(h) * D + 8 * (lane >> 5);
 #pragma unroll
     for (int c = 0; c < QF; ++c) {
       uint4 u = make_uint4(0, 0, 0, 0);
-      if (valid) u = *reinterpret_cast<const uint4*>(qrow + 16 * c + base);
+      if (qrow < a.Nq) u = *reinterpret_cast<const uint4*>(qp + 16 * c);
       qf[c] = __builtin_bit_cast(typename E::vec8, u);
     }
   }
 
-  __device__ __forceinline__ void stage_load(const In* kb, const In* vb, int64_t rs, int k0,
-                                             int nk, int tid) {
+  int last_key = a.Nk - 1;
+  int wave_last = a.Nk - 1;
+  if (CAUSAL) {
+    last_key = min(last_key, q0 + BR - 1 + a.off);
+    wave_last = min(wave_last, qw0 + kQPW - 1 + a.off);
+  }
+  const int n_tiles = last_key >= 0 ? last_key / kBC + 1 : 0;
+
+  // Per-lane LDS read geometry.
+  const int kr = lane & 31;                 // K operand row within a 32-key block
+  const int ksw = swz<D>(kr);
+  const int khi = lane >> 5;
+  const int blk = lane >> 4, r16 = lane & 15;
+  const int vrow = 4 * (blk >> 1) + (r16 >> 2);          // 0..7
+  const int vsw0 = swz<D>(vrow), vsw1 = swz<D>(vrow + 8);
+  const int vcl = 2 * (blk & 1) + ((r16 & 3) >> 1);      // chunk within a 32-wide d block
+  const int vin = (r16 & 1) * 4;                          // element within the chunk
+
+  f32x16 acc[D / 32];
 #pragma unroll
-    for (int r = 0; r < PER_THREAD; ++r) {
-      const int ci = tid + r * kThreads;
-      const int key = k0 + ci / CPR, dc = ci % CPR;
-      uint4 ku = make_uint4(0, 0, 0, 0), vu = make_uint4(0, 0, 0, 0);
-      if (key < nk) {
-        ku = *reinterpret_cast<const uint4*>(kb + key * rs + dc * 8);
-        vu = *reinterpret_cast<const uint4*>(vb + key * rs + dc * 8);
+  for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
+  float m_run = kNegInf, m2_run = kNegInf, l_run = 0.f;   // this lane's query row
+
+  if (n_tiles > 0)
+    load_kv_tile<D, NW>(kbase, vbase, kv_rs, 0, a.Nk, &smem[0][0][0], &smem[0][1][0], wave, lane);
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  for (int j = 0; j < n_tiles; ++j) {
+    const int k0 = j * kBC;
+    const int buf = j & 1;
+    if (j + 1 < n_tiles)
+      load_kv_tile<D, NW>(kbase, vbase, kv_rs, k0 + kBC, a.Nk, &smem[buf ^ 1][0][0],
+                          &smem[buf ^ 1][1][0], wave, lane);
+    if (k0 <= wave_last) {
+      const uint16_t* kl = &smem[buf][0][0];
+      const uint16_t* vl = &smem[buf][1][0];
+      f32x16 s[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        f32x16 t = {};
+        const uint16_t* row = kl + (32 * kb + kr) * D;
+#pragma unroll
+        for (int c = 0; c < QF; ++c) {
+          const auto op = *reinterpret_cast<const typename E::vec8*>(
+              row + (((2 * c + khi) ^ ksw) * 8));
+          t = E::mma32(op, qf[c], t);
+        }
+        s[kb] = t;
       }
-      kst[r] = ku;
-      vst[r] = vu;
-    }
-  }
 
-  __device__ __forceinline__ void stage_store(unsigned char* buf, int tid) {
-    In* kl = reinterpret_cast<In*>(buf);
-    In* vl = kl + K_ELEMS;
+      const bool need_mask = (k0 + kBC > a.Nk) || (CAUSAL && k0 + kBC - 1 > qw0 + a.off);
+      if (need_mask) {
+        const int lim = CAUSAL ? min(a.Nk - 1, qrow + a.off) : a.Nk - 1;
 #pragma unroll
-    for (int r = 0; r < PER_THREAD; ++r) {
-      const int ci = tid + r * kThreads;
-      const int key = ci / CPR, dc = ci % CPR;
-      *reinterpret_cast<uint4*>(kl + key * KS + dc * 8) = kst[r];
-      *reinterpret_cast<uint4*>(vl + key * VS + dc * 8) = vst[r];
-    }
-  }
-
-  // s[kb] = S^T rows 32kb..32kb+31 (keys) x 32 query rows of this wave.
-  __device__ __forceinline__ void scores(const unsigned char* buf, int lane, f32x16 s[2]) const {
-    const In* kl = reinterpret_cast<const In*>(buf);
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x16 acc = {};
-      const In* row = kl + (32 * kb + (lane & 31)) * KS + 8 * (lane >> 5);
-#pragma unroll
-      for (int c = 0; c < QF; ++c) {
-        const auto a = *reinterpret_cast<const typename E::vec8*>(row + 16 * c);
-        acc = E::mma32(a, qf[c], acc);
+          for (int i = 0; i < 16; ++i) {
+            const int key = k0 + 32 * kb + 8 * (i >> 2) + 4 * khi + (i & 3);
+            if (key > lim) s[kb][i] = kNegInf;
+          }
       }
-      s[kb] = acc;
-    }
-  }
 
-  // acc[db] += V^T[32db.., keys] P^T[keys, rows]. Register i of p[kb] holds
-  // key 32kb + 8(i/4) + 4(l/32) + i%4; the P V contraction takes them 8 at a
-  // time (registers 8hh..8hh+7) and fetches V^T for exactly those keys with
-  // two transposed LDS reads.
-  __device__ __forceinline__ void pv(const unsigned char* buf, int lane, const f32x16 p[2],
-                                     f32x16* acc) const {
-    const In* vl = reinterpret_cast<const In*>(buf) + K_ELEMS;
-    const int blk = lane >> 4, r = lane & 15;
-    const int dlane = 16 * (blk & 1) + 4 * (r & 3);
-    const int klane = 4 * (blk >> 1) + (r >> 2);
+      float mx = kNegInf;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int o = 8 * hh;
-        const auto bop = pack8<E>(p[kb][o + 0], p[kb][o + 1], p[kb][o + 2], p[kb][o + 3],
-                                  p[kb][o + 4], p[kb][o + 5], p[kb][o + 6], p[kb][o + 7]);
-        const In* rowp = vl + (32 * kb + 16 * hh + klane) * VS + dlane;
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+      mx = max_xor32(mx);
+      // Exact running max: the largest probability of the row is exactly 1,
+      // so it passes the rounding of P to the input type unchanged.
+      const float m_new = fmaxf(m_run, mx);
+      const float m2_new = m_new * a.c;
+      const float m2_use = (m_new == kNegInf) ? 0.f : m2_new;
+      const float alpha = (m_new == m_run) ? 1.f : exp2_fast(m2_run - m2_new);
+      if (__any(alpha != 1.f)) {
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const In* a0 = rowp + 32 * db;
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(a0));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(a0 + 8 * VS));
-          typedef short i16x8 __attribute__((ext_vector_type(8)));
-          const i16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          acc[db] = E::mma32(__builtin_bit_cast(typename E::vec8, w), bop, acc[db]);
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+      }
+      float rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = exp2_fast(fmaf(s[kb][i], a.c, -m2_use));
+          s[kb][i] = p;
+          rs += p;
+        }
+      l_run = fmaf(alpha, l_run, rs);
+      m_run = m_new;
+      m2_run = m2_new;
+
+      // O^T += V^T P^T, keys in the order the score layout holds them.
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int o = 8 * hh;
+          const auto bop = pack8<E>(s[kb][o + 0], s[kb][o + 1], s[kb][o + 2], s[kb][o + 3],
+                                    s[kb][o + 4], s[kb][o + 5], s[kb][o + 6], s[kb][o + 7]);
+          const uint16_t* r0 = vl + (32 * kb + 16 * hh + vrow) * D + vin;
+          const uint16_t* r1 = r0 + 8 * D;
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            const int ch = 4 * db + vcl;
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) i16x4*)(r0 + ((ch ^ vsw0) * 8)));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) i16x4*)(r1 + ((ch ^ vsw1) * 8)));
+            typedef short i16x8 __attribute__((ext_vector_type(8)));
+            const i16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            acc[db] = E::mma32(__builtin_bit_cast(typename E::vec8, w), bop, acc[db]);
+          }
         }
       }
     }
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
   }
-};
+
+  const float l_tot = sum_xor32(l_run);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (qrow < a.Nq) {
+    OutT* orow = static_cast<OutT*>(a.o) + (static_cast<int64_t>(b) * a.Nq + qrow) * q_rs +
+                 static_cast<int64_t>(h) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        store4(orow + 32 * db + 8 * g + 4 * khi, acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv,
+               acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv);
+    if (lane < 32)
+      a.lse[(static_cast<int64_t>(b) * a.H + h) * a.Nq + qrow] =
+          l_tot > 0.f ? (m2_run + log2f(l_tot)) * kLn2 : kNegInf;
+  }
+}
 
 // ---------------------------------------------------------------------------
 // fp32 inputs: 32x32x2 fp32 matrix-core ops, probabilities kept in fp32.
@@ -381,16 +492,29 @@ hipError_t launch_t(const FwdParams& p, bool causal, hipStream_t s) {
   return hipGetLastError();
 }
 
+constexpr int kNW16 = 4;   // waves per workgroup of the 16-bit kernel
+
+template <class E, typename OutT, int D>
+hipError_t launch16(const FwdParams& p, bool causal, hipStream_t s) {
+  if (causal)
+    hipLaunchKernelGGL((fwd16_kernel<E, OutT, D, true, kNW16>), dim3(p.total), dim3(kNW16 * 64),
+                       0, s, p);
+  else
+    hipLaunchKernelGGL((fwd16_kernel<E, OutT, D, false, kNW16>), dim3(p.total), dim3(kNW16 * 64),
+                       0, s, p);
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t dispatch_d(const FwdParams& p, const ForwardArgs& a, hipStream_t s) {
   const bool c = a.causal != 0;
   switch (a.in_dtype) {
     case FA_BF16:
-      return a.out_dtype == FA_F32 ? launch_t<Policy16<BF16, D>, float, D>(p, c, s)
-                                   : launch_t<Policy16<BF16, D>, __bf16, D>(p, c, s);
+      return a.out_dtype == FA_F32 ? launch16<BF16, float, D>(p, c, s)
+                                   : launch16<BF16, __bf16, D>(p, c, s);
     case FA_F16:
-      return a.out_dtype == FA_F32 ? launch_t<Policy16<F16, D>, float, D>(p, c, s)
-                                   : launch_t<Policy16<F16, D>, _Float16, D>(p, c, s);
+      return a.out_dtype == FA_F32 ? launch16<F16, float, D>(p, c, s)
+                                   : launch16<F16, _Float16, D>(p, c, s);
     case FA_F32:
       return launch_t<PolicyF32<D>, float, D>(p, c, s);
   }
@@ -404,7 +528,8 @@ hipError_t launch_forward(const ForwardArgs& a, hipStream_t s) {
   p.q = a.q; p.k = a.k; p.v = a.v; p.o = a.o; p.lse = a.lse;
   p.B = a.B; p.H = a.H; p.Hkv = a.Hkv; p.Nq = a.Nq; p.Nk = a.Nk;
   p.group = a.H / a.Hkv;
-  p.n_qblocks = (a.Nq + kBR - 1) / kBR;
+  const int br = a.in_dtype == FA_F32 ? kBR : kNW16 * kQPW;
+  p.n_qblocks = (a.Nq + br - 1) / br;
   p.total = a.B * a.H * p.n_qblocks;
   p.c = a.scale * kLog2e;
   p.off = a.Nk - a.Nq;
