@@ -128,24 +128,29 @@ def main():
     dp = inputs.WORKLOADS[DECODE].params
     B, H, N, d = pp["B"], pp["H"], pp["N"], pp["d"]
 
-    log(f"bench: generating {PREFILL} inputs")
-    q, k, v = inputs.prefill_inputs(B, H, pp["Hkv"], N, N, d, torch.bfloat16, pp["seed"])
-    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
-    o = torch.empty_like(qd)
-    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
     flops = causal_flops(B, H, N, d)
+    if "prefill" in parts or args.cpu_seconds > 0:
+        log(f"bench: generating {PREFILL} inputs")
+        q, k, v = inputs.prefill_inputs(B, H, pp["Hkv"], N, N, d, torch.bfloat16, pp["seed"])
+    if "prefill" in parts:
+        qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+        o = torch.empty_like(qd)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
 
-    log(f"bench: generating {DECODE} inputs")
     lens = inputs.uniform_lengths(dp["B"], dp["len_lo"], dp["len_hi"], dp["seed"])
-    pi = inputs.paged_decode_inputs(dp["B"], dp["H"], dp["Hkv"], dp["d"], lens, dp["seed"],
-                                    pool_factor=dp["pool_factor"], max_pages=dp["len_hi"] // 16)
-    dq, dk, dv = pi.q.to(dev), pi.k_pool.to(dev), pi.v_pool.to(dev)
-    dt_, ds_ = pi.block_table.to(dev), pi.seq_lens.to(dev)
-    od = torch.empty_like(dq)
-    lsed = torch.empty((dp["B"], dp["H"]), dtype=torch.float32, device=dev)
-    ws = torch.empty(fa.decode_workspace_size(dp["B"], dp["H"], dp["d"], fa.MAX_SPLITS),
-                     dtype=torch.uint8, device=dev)
     kv_bytes = float(lens.sum()) * dp["Hkv"] * dp["d"] * 2 * 2
+    if "decode" in parts or args.cpu_seconds > 0:
+        log(f"bench: generating {DECODE} inputs")
+        pi = inputs.paged_decode_inputs(dp["B"], dp["H"], dp["Hkv"], dp["d"], lens, dp["seed"],
+                                        pool_factor=dp["pool_factor"],
+                                        max_pages=dp["len_hi"] // 16)
+    if "decode" in parts:
+        dq, dk, dv = pi.q.to(dev), pi.k_pool.to(dev), pi.v_pool.to(dev)
+        dt_, ds_ = pi.block_table.to(dev), pi.seq_lens.to(dev)
+        od = torch.empty_like(dq)
+        lsed = torch.empty((dp["B"], dp["H"]), dtype=torch.float32, device=dev)
+        ws = torch.empty(fa.decode_workspace_size(dp["B"], dp["H"], dp["d"], fa.MAX_SPLITS),
+                         dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     def step(ev=None):
@@ -207,7 +212,7 @@ def main():
         "roofline": None if pre_tflops is None else {
             "bound": "mfma", "achieved": pre_tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s", "frac": pre_tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
-            "kernel": "fwd_kernel<Policy16<BF16,128>,bf16,128,causal>",
+            "kernel": "fwd16_kernel<BF16, bf16 out, d=128, causal, 4 waves>",
             "ms_mean": float(pre_ms.mean()), "ms_min": float(pre_ms.min()),
             "algorithmic_flop_per_launch": flops},
         "decode": None if dec_gbps is None else {

@@ -9,20 +9,24 @@
 // times. Pages are found through the block table ("Paged and ragged layouts:
 // FlashInfer").
 //
-// Decode kernel, one workgroup (4 waves) per (sequence, KV head, chunk):
-//   * wave w streams pages w, w+4, ... of the chunk; the next page's K and V
-//     are loaded while the current one is processed;
-//   * scores: S^T (16 tokens x 16 head slots) = K_page Q^T on a 16x16x32
-//     matrix-core op, K loaded straight from HBM into the operand registers
-//     (each lane 16 bytes of one token row); lane l then holds head l % 16
-//     for tokens 4(l/16)..4(l/16)+3, only the first G head slots are real;
-//   * online softmax per head with two cross-row exchanges (l^16, l^32);
-//   * P V on the vector ALUs: the page's probabilities and rescale factors
-//     go through a small per-wave LDS buffer to lanes that own 8 contiguous
-//     d of a few token rows, V read with 16-byte coalesced loads;
-//   * at the end the 4 wave states are merged in LDS with the same rule and
-//     the chunk's (o, lse) is written: as the final output when the sequence
-//     has one chunk, else as a partial for the merge kernel.
+// The decode is bound by HBM bandwidth, so the design is about keeping many
+// bytes in flight per CU with little register cost:
+//   * one workgroup (4 waves) per (sequence, KV head, chunk); wave w takes
+//     pages w, w+4, ... of the chunk;
+//   * each wave streams its pages through a private ring of kStages page
+//     slots in LDS with direct-to-LDS loads (global_load_lds_dwordx4): three
+//     pages are in flight while one is processed, and no VGPR holds data in
+//     transit. The chunk's page ids are staged in LDS first;
+//   * scores: S^T (16 tokens x 16 head slots) = K_page Q^T on one 16x16x32
+//     matrix-core op per 32 of d; lane l holds head slot l % 16 for tokens
+//     4(l/16) .. 4(l/16)+3, only the first G head slots are real;
+//   * online softmax per head, two cross-row exchanges (l^16, l^32);
+//   * P V on the vector ALUs: probabilities and rescale factors reach the
+//     lanes that own 8 contiguous d of a few token rows through a per-wave
+//     LDS scratch;
+//   * finally the 4 wave states are merged in LDS by the same rule and the
+//     chunk's (o, lse) is written: as the output when the sequence has one
+//     chunk, else as a partial for the merge kernel.
 // Merge kernel, one wave per (sequence, head): M = max lse, weights e^(lse-M),
 // fixed summation order, no atomics.
 #include "fa_device.hpp"
@@ -35,6 +39,8 @@ namespace {
 constexpr int kDecWaves = 4;
 constexpr int kDecThreads = kDecWaves * 64;
 constexpr int kPage = FA_PAGE_SIZE;   // 16 token slots per page
+constexpr int kStages = 2;            // page slots per wave ring (2 workgroups fit a CU)
+constexpr int kIdBatch = 1024;        // page ids staged in LDS at a time
 
 struct DecParams {
   const uint16_t* q;
@@ -52,18 +58,71 @@ struct DecParams {
 
 __device__ __forceinline__ float nanf_() { return __builtin_nanf(""); }
 
+// K rows in the ring have their 16-byte chunks permuted by an XOR with
+// kswz(row) so that the 16 lanes reading one chunk of 16 token rows hit 16
+// different bank groups.
+template <int D>
+__device__ __forceinline__ int kswz(int row) {
+  return D == 128 ? row : (row >> 1) & 7;
+}
+
+template <int D>
+struct DecGeom {
+  static constexpr int CPR = D / 8;                  // 16-byte chunks per token row
+  static constexpr int PAGE_ELEMS = kPage * D;       // one head's K (or V) of one page
+  static constexpr int SLABS = PAGE_ELEMS * 2 / 1024; // 1 KiB wave-loads per tensor per page
+  static constexpr int SLOT_ELEMS = 2 * PAGE_ELEMS;  // ring slot: K then V
+  static constexpr int RING_ELEMS = kStages * SLOT_ELEMS;
+  static constexpr int LPR = D / 8;                  // lanes per token row in the P V layout
+  static constexpr int RPI = 64 / LPR;               // token rows per 16-byte load instruction
+  static constexpr int TPL = kPage / RPI;            // token rows per lane per page
+  static constexpr int NC = D / 32;                  // 16x16x32 steps over d
+};
+
+// One wave's direct-to-LDS loads of one page (K then V of one KV head) into
+// a ring slot.
+template <int D>
+struct PageLoader {
+  using Geo = DecGeom<D>;
+  int koff[Geo::SLABS], voff[Geo::SLABS];   // element offsets from the page base
+
+  // Slab s of K fills ring slots 64s + lane (chunks permuted by kswz); V
+  // slots are not permuted.
+  __device__ __forceinline__ PageLoader(int64_t row_stride, int lane) {
+#pragma unroll
+    for (int s = 0; s < Geo::SLABS; ++s) {
+      const int slot = s * 64 + lane;
+      const int row = slot / Geo::CPR, ch = slot % Geo::CPR;
+      koff[s] = static_cast<int>(row * row_stride) + ((ch ^ kswz<D>(row)) * 8);
+      voff[s] = static_cast<int>(row * row_stride) + ch * 8;
+    }
+  }
+
+  __device__ __forceinline__ void issue(const uint16_t* kbase, const uint16_t* vbase,
+                                        int64_t page_stride, int page_id, uint16_t* slot) const {
+    const int pg = __builtin_amdgcn_readfirstlane(page_id);
+    const int64_t pbase = static_cast<int64_t>(pg) * page_stride;
+#pragma unroll
+    for (int s = 0; s < Geo::SLABS; ++s)
+      load_lds16(kbase + pbase + koff[s], slot + s * 512);
+#pragma unroll
+    for (int s = 0; s < Geo::SLABS; ++s)
+      load_lds16(vbase + pbase + voff[s], slot + Geo::PAGE_ELEMS + s * 512);
+  }
+};
+
 template <class E, typename OutT, int D, int G>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecParams a) {
-  constexpr int LPR = D / 8;           // lanes per token row in the P V layout
-  constexpr int RPI = 64 / LPR;        // token rows covered per 16-byte load instruction
-  constexpr int TPL = kPage / RPI;     // token rows per lane per page
-  constexpr int NC = D / 32;           // 16x16x32 steps over d
+  using Geo = DecGeom<D>;
   static_assert(G >= 1 && G <= 16, "head group must fit the 16 head slots");
+  static_assert(kDecWaves * G * D * 4 <= kDecWaves * Geo::RING_ELEMS * 2,
+                "wave states must fit in the ring for the final merge");
 
-  __shared__ float pbuf[kDecWaves][G][kPage];   // per-wave probabilities [head][token]
-  __shared__ float abuf[kDecWaves][G];          // per-wave rescale factors
+  __shared__ __attribute__((aligned(16))) uint16_t ring[kDecWaves][Geo::RING_ELEMS];
+  __shared__ int ids[kIdBatch];
+  __shared__ __attribute__((aligned(16))) float pbuf[kDecWaves][G][kPage];  // [head][token]
+  __shared__ float abuf[kDecWaves][G];
   __shared__ float wm[kDecWaves][G], wl[kDecWaves][G];
-  __shared__ float wacc[kDecWaves][G][D];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
@@ -84,19 +143,22 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecParams a) 
   // Q^T operand: lane l holds q[b, hk*G + l%16, 32c + 8(l/16) + j] (zero for
   // head slots >= G).
   const int hs = lane & 15, grp = lane >> 4;
-  typename E::vec8 qop[NC];
+  typename E::vec8 qop[Geo::NC];
   {
     const uint16_t* qrow = a.q + (static_cast<int64_t>(b) * a.H + hk * G + hs) * D + 8 * grp;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
+    for (int c = 0; c < Geo::NC; ++c) {
       uint4 u = make_uint4(0, 0, 0, 0);
       if (hs < G) u = *reinterpret_cast<const uint4*>(qrow + 32 * c);
       qop[c] = __builtin_bit_cast(typename E::vec8, u);
     }
   }
 
-  // P V layout: lane owns d = 8e..8e+7 of token rows r*TPL .. r*TPL+TPL-1.
-  const int e = lane % LPR, r = lane / LPR;
+  const PageLoader<D> loader(row_stride, lane);
+  // Per-lane read geometry: K operand (token hs, chunk 4c + grp) and the
+  // P V layout (d = 8e .. 8e+7 of token rows r*TPL .. r*TPL+TPL-1).
+  const int e = lane % Geo::LPR, r = lane / Geo::LPR;
+  uint16_t* my_ring = &ring[wave][0];
 
   float acc[G][8];
 #pragma unroll
@@ -106,113 +168,109 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecParams a) 
   float m_run = kNegInf, m2_run = kNegInf, l_run = 0.f;   // head slot hs
   bool bad_page = false;
 
-  uint4 kc[NC], vc[TPL], kn[NC], vn[TPL];
-  auto load_page = [&](int pg, uint4* kd, uint4* vd) {
-    const uint16_t* kp = kbase + static_cast<int64_t>(pg) * page_stride;
-    const uint16_t* vp = vbase + static_cast<int64_t>(pg) * page_stride;
-#pragma unroll
-    for (int c = 0; c < NC; ++c)
-      kd[c] = *reinterpret_cast<const uint4*>(kp + hs * row_stride + 32 * c + 8 * grp);
-#pragma unroll
-    for (int i = 0; i < TPL; ++i)
-      vd[i] = *reinterpret_cast<const uint4*>(vp + (r * TPL + i) * row_stride + 8 * e);
-  };
-
-  const int my_first = pb + wave;
-  const int my_count = my_first < pe ? (pe - my_first + kDecWaves - 1) / kDecWaves : 0;
-
-  // Page ids of this wave, 64 at a time, one per lane; read back with readlane.
-  int ids = 0;
-  auto fetch_ids = [&](int k0) {
-    const int kk = k0 + lane;
-    int v = 0;
-    if (kk < my_count) v = table[my_first + kk * kDecWaves];
-    ids = v;
-  };
-  auto page_id = [&](int k) -> int {
-    int v = __builtin_amdgcn_readlane(ids, k & 63);
-    if (v < 0 || v >= a.num_pages) {   // outside the pool: never dereferenced
-      bad_page = true;
-      v = 0;
-    }
-    return v;
-  };
-
-  if (my_count > 0) {
-    fetch_ids(0);
-    load_page(page_id(0), kc, vc);
-  }
-  for (int k = 0; k < my_count; ++k) {
-    const int p = my_first + k * kDecWaves;
-    if (k + 1 < my_count) {
-      if (((k + 1) & 63) == 0) fetch_ids(k + 1);
-      load_page(page_id(k + 1), kn, vn);
-    }
-    // Scores for 16 tokens x 16 head slots.
-    f32x4 s = {};
-#pragma unroll
-    for (int c = 0; c < NC; ++c) s = E::mma16(__builtin_bit_cast(typename E::vec8, kc[c]), qop[c], s);
-    const int t0 = p * kPage;                 // first token of the page
-    const int valid = min(kPage, len - t0);   // tokens of this page that exist
-    if (valid < kPage) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (4 * grp + i >= valid) s[i] = kNegInf;
-    }
-    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-    mx = max_xor16(mx);
-    mx = max_xor32(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float m2_new = m_new * a.c;
-    const float m2_use = (m_new == kNegInf) ? 0.f : m2_new;
-    const float alpha = (m_new == m_run) ? 1.f : exp2_fast(m2_run - m2_new);
-    float pr[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) pr[i] = exp2_fast(fmaf(s[i], a.c, -m2_use));
-    l_run = fmaf(alpha, l_run, (pr[0] + pr[1]) + (pr[2] + pr[3]));
-    m_run = m_new;
-    m2_run = m2_new;
-    if (hs < G) {
-      *reinterpret_cast<float4*>(&pbuf[wave][hs][4 * grp]) = make_float4(pr[0], pr[1], pr[2], pr[3]);
-      if (grp == 0) abuf[wave][hs] = alpha;
-    }
-    // The writes above and the reads below are this wave's own LDS traffic;
-    // LDS operations of one wave complete in order once issued.
-    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-
-    // acc[n][:] = alpha_n acc[n][:] + sum_t p[n][t] V[t][8e..8e+7]
-    float vv[TPL][8];
-#pragma unroll
-    for (int i = 0; i < TPL; ++i) {
-      const bool ok = r * TPL + i < valid;
-      const uint32_t w[4] = {vc[i].x, vc[i].y, vc[i].z, vc[i].w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        vv[i][2 * j] = ok ? E::to_f32(static_cast<uint16_t>(w[j] & 0xffffu)) : 0.f;
-        vv[i][2 * j + 1] = ok ? E::to_f32(static_cast<uint16_t>(w[j] >> 16)) : 0.f;
+  for (int b0 = pb; b0 < pe; b0 += kIdBatch) {
+    const int bn = min(kIdBatch, pe - b0);
+    if (b0 != pb) __syncthreads();   // previous batch's ids no longer read
+    for (int x = tid; x < bn; x += kDecThreads) {
+      int id = table[b0 + x];
+      if (id < 0 || id >= a.num_pages) {   // outside the pool: never dereferenced
+        bad_page = true;
+        id = 0;
       }
+      ids[x] = id;
     }
-#pragma unroll
-    for (int n = 0; n < G; ++n) {
-      const float al = abuf[wave][n];
-      float pn[TPL];
-#pragma unroll
-      for (int i = 0; i < TPL; ++i) pn[i] = pbuf[wave][n][r * TPL + i];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float x = acc[n][j] * al;
-#pragma unroll
-        for (int i = 0; i < TPL; ++i) x = fmaf(pn[i], vv[i][j], x);
-        acc[n][j] = x;
+    __syncthreads();
+
+    const int cnt = wave < bn ? (bn - wave + kDecWaves - 1) / kDecWaves : 0;
+    for (int k = 0; k < min(kStages - 1, cnt); ++k)
+      loader.issue(kbase, vbase, page_stride, ids[wave + k * kDecWaves],
+                   my_ring + (k % kStages) * Geo::SLOT_ELEMS);
+
+    for (int k = 0; k < cnt; ++k) {
+      if (k + kStages - 1 < cnt) {
+        const int kk = k + kStages - 1;
+        loader.issue(kbase, vbase, page_stride, ids[wave + kk * kDecWaves],
+                     my_ring + (kk % kStages) * Geo::SLOT_ELEMS);
       }
-    }
-    if (k + 1 < my_count) {
+      // Wait for page k: the loads of the pages issued after it may stay
+      // in flight (2 * SLABS instructions per page).
+      const int after = min(kStages - 1, cnt - 1 - k);
+      if (after >= 3) {
+        __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * 2 * Geo::SLABS) : "memory");
+      } else if (after == 2) {
+        __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * 2 * Geo::SLABS) : "memory");
+      } else if (after == 1) {
+        __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * Geo::SLABS) : "memory");
+      } else {
+        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      const uint16_t* kl = my_ring + (k % kStages) * Geo::SLOT_ELEMS;
+      const uint16_t* vl = kl + Geo::PAGE_ELEMS;
+      const int p = b0 + wave + k * kDecWaves;   // page index within the sequence
+
+      // Scores for 16 tokens x 16 head slots.
+      f32x4 s = {};
 #pragma unroll
-      for (int c = 0; c < NC; ++c) kc[c] = kn[c];
+      for (int c = 0; c < Geo::NC; ++c) {
+        const auto op = *reinterpret_cast<const typename E::vec8*>(
+            kl + hs * D + (((4 * c + grp) ^ kswz<D>(hs)) * 8));
+        s = E::mma16(op, qop[c], s);
+      }
+      const int valid = min(kPage, len - p * kPage);   // tokens of this page that exist
+      if (valid < kPage) {
 #pragma unroll
-      for (int i = 0; i < TPL; ++i) vc[i] = vn[i];
+        for (int i = 0; i < 4; ++i)
+          if (4 * grp + i >= valid) s[i] = kNegInf;
+      }
+      float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+      mx = max_xor16(mx);
+      mx = max_xor32(mx);
+      const float m_new = fmaxf(m_run, mx);
+      const float m2_new = m_new * a.c;
+      const float m2_use = (m_new == kNegInf) ? 0.f : m2_new;
+      const float alpha = (m_new == m_run) ? 1.f : exp2_fast(m2_run - m2_new);
+      float pr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pr[i] = exp2_fast(fmaf(s[i], a.c, -m2_use));
+      l_run = fmaf(alpha, l_run, (pr[0] + pr[1]) + (pr[2] + pr[3]));
+      m_run = m_new;
+      m2_run = m2_new;
+      if (hs < G) {
+        *reinterpret_cast<float4*>(&pbuf[wave][hs][4 * grp]) = make_float4(pr[0], pr[1], pr[2], pr[3]);
+        if (grp == 0) abuf[wave][hs] = alpha;
+      }
+      // The writes above and the reads below are this wave's own LDS traffic,
+      // completed in issue order.
+      __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+
+      // acc[n][:] = alpha_n acc[n][:] + sum_t p[n][t] V[t][8e..8e+7]
+#pragma unroll
+      for (int n = 0; n < G; ++n) {
+        const float al = abuf[wave][n];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[n][j] *= al;
+      }
+#pragma unroll
+      for (int i = 0; i < Geo::TPL; ++i) {
+        const int t = r * Geo::TPL + i;
+        const uint4 raw = *reinterpret_cast<const uint4*>(vl + t * D + 8 * e);
+        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+        float vv[8];
+        const bool ok = t < valid;   // slots past the end may hold anything
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          vv[2 * j] = ok ? E::to_f32(static_cast<uint16_t>(w[j] & 0xffffu)) : 0.f;
+          vv[2 * j + 1] = ok ? E::to_f32(static_cast<uint16_t>(w[j] >> 16)) : 0.f;
+        }
+#pragma unroll
+        for (int n = 0; n < G; ++n) {
+          const float pn = pbuf[wave][n][t];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[n][j] = fmaf(pn, vv[j], acc[n][j]);
+        }
+      }
+      __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
-    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   }
 
   // Wave totals: l over the four token groups, acc over the token rows.
@@ -223,12 +281,16 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecParams a) 
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       float x = acc[n][j];
-      if (RPI == 8) x += __uint_as_float(__builtin_amdgcn_update_dpp(
-                         0u, __float_as_uint(x), 0x128, 0xf, 0xf, false));   // row_ror:8
+      if (Geo::RPI == 8) x += __uint_as_float(__builtin_amdgcn_update_dpp(
+                              0u, __float_as_uint(x), 0x128, 0xf, 0xf, false));   // row_ror:8
       x = sum_xor16(x);
       x = sum_xor32(x);
       acc[n][j] = x;
     }
+  // The ring is free once every wave has passed this barrier; the wave
+  // states are merged in its memory.
+  const bool bad = bad_len || __syncthreads_or(bad_page);
+  float* wacc = reinterpret_cast<float*>(&ring[0][0]);   // [wave][G][D]
   if (lane < G) {
     wm[wave][lane] = m2_run;
     wl[wave][lane] = l_tot;
@@ -237,11 +299,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecParams a) 
 #pragma unroll
     for (int n = 0; n < G; ++n)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) wacc[wave][n][8 * e + j] = acc[n][j];
+      for (int j = 0; j < 8; ++j) wacc[(wave * G + n) * D + 8 * e + j] = acc[n][j];
   }
-  const bool bad = bad_len || __syncthreads_or(bad_page);
+  __syncthreads();
 
-  // Merge the four wave states and write the chunk result.
   const bool final_out = nsplit == 1;
   for (int x = tid; x < G * D; x += kDecThreads) {
     const int n = x / D, dd = x % D;
@@ -254,7 +315,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecParams a) 
       for (int w = 0; w < kDecWaves; ++w) {
         const float wt = exp2_fast(wm[w][n] - M);
         lsum = fmaf(wt, wl[w][n], lsum);
-        osum = fmaf(wt, wacc[w][n][dd], osum);
+        osum = fmaf(wt, wacc[(w * G + n) * D + dd], osum);
       }
     }
     float o = lsum > 0.f ? osum / lsum : 0.f;
@@ -273,7 +334,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecParams a) 
 }
 
 // ---------------------------------------------------------------------------
-// Merge: one wave per row.
+// Merge: one wave per row. The row's weights are formed once (lane c owns
+// part c) and broadcast through LDS; every output element then sums its
+// parts in index order.
 // ---------------------------------------------------------------------------
 struct MergeParams {
   const float* o_parts;
@@ -288,10 +351,13 @@ struct MergeParams {
   int max_len;                // decode mode: max_pages * page_size
 };
 
+constexpr int kMergeMaxS = 1024;
+
 template <typename OutT, bool DECODE>
 __global__ __launch_bounds__(256) void merge_kernel(const MergeParams a) {
-  const int lane = threadIdx.x & 63;
-  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  __shared__ float wsh[4][DECODE ? FA_MAX_SPLITS : kMergeMaxS];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + wave;
   if (r >= a.R) return;
   int n;
   if (DECODE) {
@@ -305,31 +371,48 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams a) {
   }
   const float* lse_r = a.lse_parts + r * a.S;
   const float* o_r = a.o_parts + r * a.S * a.d;
+  OutT* out = static_cast<OutT*>(a.o) + r * a.d;
+
+  // M = max over the parts; a NaN part poisons the row instead of vanishing
+  // in the max.
   float M = kNegInf;
   bool has_nan = false;
-  for (int c = 0; c < n; ++c) {
+  for (int c = lane; c < n; c += 64) {
     const float v = lse_r[c];
     has_nan |= v != v;
     M = fmaxf(M, v);
   }
-  OutT* out = static_cast<OutT*>(a.o) + r * a.d;
-  if (has_nan) {   // a flagged part poisons the row instead of vanishing in the max
-    for (int x = lane; x < a.d; x += 64) store1(out + x, nanf_());
-    if (lane == 0) a.lse[r] = nanf_();
-    return;
-  }
-  if (M == kNegInf) {
-    for (int x = lane; x < a.d; x += 64) store1(out + x, 0.f);
-    if (lane == 0) a.lse[r] = kNegInf;
+  M = max_xor32(M);
+#pragma unroll
+  for (int sh = 16; sh >= 1; sh >>= 1) M = fmaxf(M, __shfl_xor(M, sh));
+  has_nan = __any(has_nan);
+  if (has_nan || M == kNegInf) {
+    const float fill = has_nan ? nanf_() : 0.f;
+    for (int x = lane; x < a.d; x += 64) store1(out + x, fill);
+    if (lane == 0) a.lse[r] = has_nan ? nanf_() : kNegInf;
     return;
   }
   float z = 0.f;
-  for (int c = 0; c < n; ++c) z += expf(lse_r[c] - M);
+  for (int c = lane; c < n; c += 64) {
+    const float w = expf(lse_r[c] - M);   // empty parts (-inf) weigh 0
+    wsh[wave][c] = w;
+    z += w;
+  }
+  z = sum_xor32(z);
+#pragma unroll
+  for (int sh = 16; sh >= 1; sh >>= 1) z += __shfl_xor(z, sh);
+  __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // own wave's LDS writes
   const float inv = 1.f / z;
   for (int x = lane; x < a.d; x += 64) {
-    float s = 0.f;
-    for (int c = 0; c < n; ++c) s = fmaf(expf(lse_r[c] - M), o_r[c * a.d + x], s);
-    store1(out + x, s * inv);
+    float acc = 0.f;
+    if (DECODE) {
+#pragma unroll
+      for (int c = 0; c < FA_MAX_SPLITS; ++c)
+        if (c < n) acc = fmaf(wsh[wave][c], o_r[c * a.d + x], acc);
+    } else {
+      for (int c = 0; c < n; ++c) acc = fmaf(wsh[wave][c], o_r[c * a.d + x], acc);
+    }
+    store1(out + x, acc * inv);
   }
   if (lane == 0) a.lse[r] = M + logf(z);
 }

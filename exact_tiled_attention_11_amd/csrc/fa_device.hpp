@@ -49,6 +49,13 @@ __device__ __forceinline__ float sum_xor16(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
+// lane i's 16 bytes land at lds + 16 * i; `lds` must be wave-uniform. The
+// explicit address-space casts keep the host compilation pass well-formed.
+__device__ __forceinline__ void load_lds16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
 // Element types. Storage is handled as raw 16-bit words; arithmetic types
 // are the compiler's __bf16 / _Float16.
 struct BF16 {
@@ -94,6 +101,15 @@ __device__ __forceinline__ typename E::vec8 pack8(float a0, float a1, float a2, 
   return r;
 }
 
+// The value is rounded to fp32 before any narrowing store: without this the
+// compiler may fuse the last multiply into a mixed-precision op that rounds
+// once, straight to fp16, and the fp16 output would no longer be exactly the
+// round-to-nearest-even of the fp32 output of the same computation.
+__device__ __forceinline__ float as_f32(float x) {
+  __asm__("" : "+v"(x));
+  return x;
+}
+
 // Output stores of 4 consecutive floats in the output element type.
 __device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
   *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
@@ -101,20 +117,22 @@ __device__ __forceinline__ void store4(float* p, float a, float b, float c, floa
 __device__ __forceinline__ void store4(__bf16* p, float a, float b, float c, float d) {
   typedef __bf16 v4 __attribute__((ext_vector_type(4)));
   v4 r;
-  r[0] = static_cast<__bf16>(a); r[1] = static_cast<__bf16>(b);
-  r[2] = static_cast<__bf16>(c); r[3] = static_cast<__bf16>(d);
+  r[0] = static_cast<__bf16>(as_f32(a)); r[1] = static_cast<__bf16>(as_f32(b));
+  r[2] = static_cast<__bf16>(as_f32(c)); r[3] = static_cast<__bf16>(as_f32(d));
   *reinterpret_cast<v4*>(p) = r;
 }
 __device__ __forceinline__ void store4(_Float16* p, float a, float b, float c, float d) {
   typedef _Float16 v4 __attribute__((ext_vector_type(4)));
   v4 r;
-  r[0] = static_cast<_Float16>(a); r[1] = static_cast<_Float16>(b);
-  r[2] = static_cast<_Float16>(c); r[3] = static_cast<_Float16>(d);
+  r[0] = static_cast<_Float16>(as_f32(a)); r[1] = static_cast<_Float16>(as_f32(b));
+  r[2] = static_cast<_Float16>(as_f32(c)); r[3] = static_cast<_Float16>(as_f32(d));
   *reinterpret_cast<v4*>(p) = r;
 }
 __device__ __forceinline__ void store1(float* p, float a) { *p = a; }
-__device__ __forceinline__ void store1(__bf16* p, float a) { *p = static_cast<__bf16>(a); }
-__device__ __forceinline__ void store1(_Float16* p, float a) { *p = static_cast<_Float16>(a); }
+__device__ __forceinline__ void store1(__bf16* p, float a) { *p = static_cast<__bf16>(as_f32(a)); }
+__device__ __forceinline__ void store1(_Float16* p, float a) {
+  *p = static_cast<_Float16>(as_f32(a));
+}
 
 // Workgroup id remap so that consecutive logical ids run on the same XCD.
 // The dispatcher hands workgroup p to XCD p % kXcds; here logical id L is

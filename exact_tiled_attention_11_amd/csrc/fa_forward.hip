@@ -71,24 +71,48 @@ __device__ __forceinline__ int swz(int row) {
   }
 }
 
+// This wave's share of one K/V tile load, straight into LDS. Slab s covers
+// the LDS chunk slots 64s .. 64s+63 (1 KiB); lane l fills slot 64s + l with
+// the global 16-byte chunk (slot % CPR) ^ swz(row) of key row slot / CPR.
 template <int D, int NW>
-__device__ __forceinline__ void load_kv_tile(const uint16_t* kbase, const uint16_t* vbase,
-                                             int64_t rs, int k0, int nk, uint16_t* kl,
-                                             uint16_t* vl, int wave, int lane) {
-  constexpr int CPR = D / 8;
-  constexpr int SLABS_PER_WAVE = kBC * CPR / 64 / NW;
+struct TileLoader {
+  static constexpr int CPR = D / 8;
+  static constexpr int SPW = kBC * CPR / 64 / NW;   // slabs per wave per tensor
+  int64_t off[SPW];   // element offset of this lane's chunk in key row k0 = 0
+  int row[SPW];
+  int slab0;
+
+  __device__ __forceinline__ TileLoader(int64_t rs, int wave, int lane) {
+    slab0 = wave * SPW;
 #pragma unroll
-  for (int r = 0; r < SLABS_PER_WAVE; ++r) {
-    const int slab = wave * SLABS_PER_WAVE + r;
-    const int slot = slab * 64 + lane;
-    const int row = slot / CPR;
-    const int chunk = (slot % CPR) ^ swz<D>(row);
-    const int64_t key = min(k0 + row, nk - 1);
-    const int64_t off = key * rs + chunk * 8;
-    __builtin_amdgcn_global_load_lds(kbase + off, kl + slab * 512, 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(vbase + off, vl + slab * 512, 16, 0, 0);
+    for (int r = 0; r < SPW; ++r) {
+      const int slot = (slab0 + r) * 64 + lane;
+      row[r] = slot / CPR;
+      off[r] = row[r] * rs + ((slot % CPR) ^ swz<D>(row[r])) * 8;
+    }
   }
-}
+
+  // Rows past the last key re-read the last key (finite data whose scores
+  // are masked to -inf, i.e. weight 0); only the ragged last tile needs it.
+  __device__ __forceinline__ void load(const uint16_t* kbase, const uint16_t* vbase, int64_t rs,
+                                       int k0, int nk, uint16_t* kl, uint16_t* vl) const {
+    const int64_t base = static_cast<int64_t>(k0) * rs;
+    if (k0 + kBC <= nk) {
+#pragma unroll
+      for (int r = 0; r < SPW; ++r) {
+        load_lds16(kbase + base + off[r], kl + (slab0 + r) * 512);
+        load_lds16(vbase + base + off[r], vl + (slab0 + r) * 512);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < SPW; ++r) {
+        const int64_t shift = static_cast<int64_t>(min(k0 + row[r], nk - 1) - k0 - row[r]) * rs;
+        load_lds16(kbase + base + off[r] + shift, kl + (slab0 + r) * 512);
+        load_lds16(vbase + base + off[r] + shift, vl + (slab0 + r) * 512);
+      }
+    }
+  }
+};
 
 template <class E, typename OutT, int D, bool CAUSAL, int NW>
 __global__ __launch_bounds__(NW * 64, 8 / NW)
@@ -156,8 +180,8 @@ void fwd16_kernel(const FwdParams a) {
   for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
   float m_run = kNegInf, m2_run = kNegInf, l_run = 0.f;   // this lane's query row
 
-  if (n_tiles > 0)
-    load_kv_tile<D, NW>(kbase, vbase, kv_rs, 0, a.Nk, &smem[0][0][0], &smem[0][1][0], wave, lane);
+  const TileLoader<D, NW> loader(kv_rs, wave, lane);
+  if (n_tiles > 0) loader.load(kbase, vbase, kv_rs, 0, a.Nk, &smem[0][0][0], &smem[0][1][0]);
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
@@ -165,23 +189,31 @@ void fwd16_kernel(const FwdParams a) {
     const int k0 = j * kBC;
     const int buf = j & 1;
     if (j + 1 < n_tiles)
-      load_kv_tile<D, NW>(kbase, vbase, kv_rs, k0 + kBC, a.Nk, &smem[buf ^ 1][0][0],
-                          &smem[buf ^ 1][1][0], wave, lane);
+      loader.load(kbase, vbase, kv_rs, k0 + kBC, a.Nk, &smem[buf ^ 1][0][0], &smem[buf ^ 1][1][0]);
     if (k0 <= wave_last) {
       const uint16_t* kl = &smem[buf][0][0];
       const uint16_t* vl = &smem[buf][1][0];
-      f32x16 s[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        f32x16 t = {};
-        const uint16_t* row = kl + (32 * kb + kr) * D;
+      // S^T = K Q^T: the two 32-key chains interleave and the K operands of
+      // step c+1 are read from LDS while step c multiplies.
+      f32x16 s[2] = {f32x16{}, f32x16{}};
+      {
+        const uint16_t* row0 = kl + kr * D;
+        const uint16_t* row1 = row0 + 32 * D;
+        using V8 = typename E::vec8;
+        V8 a0 = *reinterpret_cast<const V8*>(row0 + ((khi ^ ksw) * 8));
+        V8 a1 = *reinterpret_cast<const V8*>(row1 + ((khi ^ ksw) * 8));
 #pragma unroll
         for (int c = 0; c < QF; ++c) {
-          const auto op = *reinterpret_cast<const typename E::vec8*>(
-              row + (((2 * c + khi) ^ ksw) * 8));
-          t = E::mma32(op, qf[c], t);
+          V8 n0 = a0, n1 = a1;
+          if (c + 1 < QF) {
+            n0 = *reinterpret_cast<const V8*>(row0 + (((2 * c + 2 + khi) ^ ksw) * 8));
+            n1 = *reinterpret_cast<const V8*>(row1 + (((2 * c + 2 + khi) ^ ksw) * 8));
+          }
+          s[0] = E::mma32(a0, qf[c], s[0]);
+          s[1] = E::mma32(a1, qf[c], s[1]);
+          a0 = n0;
+          a1 = n1;
         }
-        s[kb] = t;
       }
 
       const bool need_mask = (k0 + kBC > a.Nk) || (CAUSAL && k0 + kBC - 1 > qw0 + a.off);

@@ -8,8 +8,11 @@
 
 namespace fa {
 
-// Tokens per split when the count is chosen automatically.
-constexpr int kSplitTokens = 2048;
+// Smallest chunk (tokens) when the count is chosen automatically: sequences
+// are cut into as many chunks of at least this many tokens as possible, up to
+// FA_MAX_SPLITS. Many small chunks keep every CU streaming until the end of
+// the launch even when sequence lengths differ by 30x.
+constexpr int kSplitTokens = 256;
 
 // Number of key chunks for a sequence of `len` tokens; `fixed` > 0 forces it.
 __host__ __device__ inline int decode_splits(int len, int fixed) {

@@ -102,9 +102,10 @@ fa_status fa_forward(const void* Q, const void* K, const void* V, void* O,
 /*
  * fa_decode_num_splits - the number of key chunks fa_decode_paged uses for a
  * sequence of seq_len tokens. num_splits > 0 forces that count;
- * num_splits == 0 picks ceil(seq_len / 2048) clamped to [1, FA_MAX_SPLITS],
- * so long sequences spread over more workgroups while short ones avoid
- * merge overhead ("3.4 Attention Kernels", "In practice": kernels choose the
+ * num_splits == 0 picks ceil(seq_len / 256) clamped to [1, FA_MAX_SPLITS]:
+ * chunks of at least 256 tokens, as many as allowed, so long and short
+ * sequences alike spread over enough workgroups to keep HBM busy to the end
+ * of the launch ("3.4 Attention Kernels", "In practice": kernels choose the
  * number of splits from the context length). Returns -1 for invalid input.
  * Pure host function; the kernels evaluate the same rule on the device.
  */

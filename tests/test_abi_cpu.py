@@ -115,8 +115,8 @@ def test_decode_workspace_checks():
 
 
 def test_split_rule_and_workspace_size():
-    assert [fa.decode_num_splits(n) for n in (0, 1, 1024, 2048, 2049, 4096, 30000, 32768, 10**6)] \
-        == [1, 1, 1, 1, 2, 2, 15, 16, 16]
+    assert [fa.decode_num_splits(n) for n in (0, 1, 256, 257, 1024, 2049, 3840, 4096, 4097, 10**6)] \
+        == [1, 1, 1, 2, 4, 9, 15, 16, 16, 16]
     assert [fa.decode_num_splits(100, s) for s in range(1, 17)] == list(range(1, 17))
     assert fa.decode_num_splits(-1) == -1 and fa.decode_num_splits(5, 17) == -1
     # fp32 o-partials, 256-byte aligned, followed by the fp32 lse-partials
