@@ -35,6 +35,29 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def sources_sha256(paths):
+    import hashlib
+    h = hashlib.sha256()
+    for rel in paths:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter runs
+    (profiles/traffic.json), or None once the kernel's sources have changed
+    since the counters were taken."""
+    try:
+        with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+            rec = json.load(f)[kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_sha256") != sources_sha256(rec["sources"]):
+        return None
+    return rec
+
+
 def causal_flops(B, H, N, d):
     return 4.0 * d * (N * (N + 1) / 2) * B * H
 
@@ -184,6 +207,7 @@ def main():
 
     pre_tflops = flops / (pre_ms.mean() * 1e-3) / 1e12 if "prefill" in parts else None
     dec_gbps = kv_bytes / (dec_ms.mean() * 1e-3) / 1e9 if "decode" in parts else None
+    tr_pre, tr_dec = measured_traffic("prefill"), measured_traffic("decode")
 
     cpu = None
     cpu_dec = None
@@ -211,7 +235,9 @@ def main():
                                                       "len_hi")} | {"splits": "auto"}},
         "roofline": None if pre_tflops is None else {
             "bound": "mfma", "achieved": pre_tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
-            "unit": "TFLOP/s", "frac": pre_tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+            "unit": "TFLOP/s", "frac": pre_tflops / MFMA_BF16_PEAK_TFLOPS,
+            "traffic": tr_pre["hbm_bytes_per_launch"] if tr_pre else None,
+            "traffic_detail": tr_pre,
             "kernel": "fwd16_kernel<BF16, bf16 out, d=128, causal, 4 waves>",
             "ms_mean": float(pre_ms.mean()), "ms_min": float(pre_ms.min()),
             "algorithmic_flop_per_launch": flops},
@@ -219,7 +245,9 @@ def main():
             "value": dec_gbps, "unit": "GB/s", "bound": "hbm", "peak": HBM_PEAK_GBPS,
             "frac": dec_gbps / HBM_PEAK_GBPS, "ms_mean": float(dec_ms.mean()),
             "ms_min": float(dec_ms.min()), "kv_bytes": kv_bytes,
-            "timed": "decode kernel + merge kernel", "traffic": None},
+            "timed": "decode kernel + merge kernel",
+            "traffic": tr_dec["hbm_bytes_per_launch"] if tr_dec else None,
+            "traffic_detail": tr_dec},
         "cpu_baseline": cpu,
         "cpu_baseline_decode": cpu_dec,
     }
