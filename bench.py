@@ -238,7 +238,7 @@ def main():
             "unit": "TFLOP/s", "frac": pre_tflops / MFMA_BF16_PEAK_TFLOPS,
             "traffic": tr_pre["hbm_bytes_per_launch"] if tr_pre else None,
             "traffic_detail": tr_pre,
-            "kernel": "fwd16_kernel<BF16, bf16 out, d=128, causal, 4 waves>",
+            "kernel": "fwd16_kernel<BF16, bf16 out, d=128, causal, 8 waves, paired query blocks>",
             "ms_mean": float(pre_ms.mean()), "ms_min": float(pre_ms.min()),
             "algorithmic_flop_per_launch": flops},
         "decode": None if dec_gbps is None else {

@@ -56,6 +56,24 @@ __device__ __forceinline__ void load_lds16(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
 }
 
+// The same copy issued from inline assembly, for kernels that track these
+// loads themselves (explicit vmcnt waits and barriers). The compiler does not
+// see the LDS write, so it adds no conservative wait for all outstanding
+// vector-memory loads in front of later LDS reads, and the caller must order
+// every read of `lds` after the copy with s_waitcnt vmcnt + a barrier. M0
+// (the LDS destination register of the copy) is saved and restored around it.
+__device__ __forceinline__ void load_lds16_async(const void* g, const void* lds) {
+  const uint32_t a = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds)));
+  uint32_t saved;
+  __asm__ volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(a)
+      : "memory");
+}
+
 // Element types. Storage is handled as raw 16-bit words; arithmetic types
 // are the compiler's __bf16 / _Float16.
 struct BF16 {

@@ -10,22 +10,26 @@
 // section "FlashAttention-2 and -3" describes). Key tiles wholly above the
 // causal diagonal are never loaded.
 //
-// Work decomposition (one workgroup = 4 waves = 128 query rows of one
-// (batch, head); one key tile = 64 keys):
-//   * Each wave owns 32 query rows. Scores are computed transposed,
-//     S^T = K Q^T, so that every lane owns ONE query row (l % 32) and 32 of
-//     the tile's keys: the row max and row sum are in-lane reductions plus
-//     one exchange with lane l ^ 32, and the per-row rescale factor is a
-//     lane-local scalar.
+// Work decomposition of the bf16/fp16 kernel (one workgroup = 8 waves, two
+// per SIMD, 32 query rows per wave; one key tile = 64 keys):
+//   * Scores are computed transposed, S^T = K Q^T, so that every lane owns ONE
+//     query row (l % 32) and 32 of the tile's keys: the row max and row sum
+//     are in-lane reductions plus one exchange with lane l ^ 32, and the
+//     per-row rescale factor is a lane-local scalar.
 //   * The score accumulator, after exponentiation and rounding to the input
 //     type, is directly the B operand of O^T += V^T P^T: no LDS round trip.
 //     The contraction over keys uses the keys in the order the score layout
 //     delivers them; V^T is fetched in that same key order.
-//   * K and V tiles are staged in LDS, double buffered: the global loads of
-//     tile j+1 are in flight while tile j is computed. V stays row-major in
-//     LDS; the transposed operand comes from ds_read_b64_tr_b16.
+//   * K and V tiles are copied from global memory straight into LDS (no
+//     register staging), one tile ahead of the one being computed. V stays
+//     row-major in LDS; the transposed operand comes from ds_read_b64_tr_b16.
+//   * Causal: a workgroup takes query blocks u and n-1-u of one head (the
+//     second with its key tiles in descending order), so all workgroups stream
+//     equally many tiles and those running together read the same tiles.
 //   * Softmax runs in base 2 with scale*log2(e) folded into one FMA; m is
 //     kept in raw-score units so LSE comes back in natural-log units.
+// fp32 inputs use a 4-wave kernel on the 32x32x2 fp32 matrix-core op with P
+// kept in fp32.
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
 
@@ -46,8 +50,9 @@ struct FwdParams {
   float* lse;
   int B, H, Hkv, Nq, Nk;
   int group;       // H / Hkv
-  int n_qblocks;   // ceil(Nq / kBR)
-  int total;       // B * H * n_qblocks
+  int n_qblocks;   // query blocks per (batch, head)
+  int units;       // workgroup work units per (batch, head)
+  int total;       // B * H * units
   float c;         // scale * log2(e)
   int off;         // Nk - Nq: key j is visible to query i iff j <= i + off
 };
@@ -94,19 +99,19 @@ struct TileLoader {
 
   // Rows past the last key re-read the last key (finite data whose scores
   // are masked to -inf, i.e. weight 0); only the ragged last tile needs it.
+  template <bool ASYNC = false>
   __device__ __forceinline__ void load(const uint16_t* kbase, const uint16_t* vbase, int64_t rs,
                                        int k0, int nk, uint16_t* kl, uint16_t* vl) const {
     const int64_t base = static_cast<int64_t>(k0) * rs;
-    if (k0 + kBC <= nk) {
 #pragma unroll
-      for (int r = 0; r < SPW; ++r) {
-        load_lds16(kbase + base + off[r], kl + (slab0 + r) * 512);
-        load_lds16(vbase + base + off[r], vl + (slab0 + r) * 512);
-      }
-    } else {
-#pragma unroll
-      for (int r = 0; r < SPW; ++r) {
-        const int64_t shift = static_cast<int64_t>(min(k0 + row[r], nk - 1) - k0 - row[r]) * rs;
+    for (int r = 0; r < SPW; ++r) {
+      int64_t shift = 0;
+      if (k0 + kBC > nk)
+        shift = static_cast<int64_t>(min(k0 + row[r], nk - 1) - k0 - row[r]) * rs;
+      if (ASYNC) {
+        load_lds16_async(kbase + base + off[r] + shift, kl + (slab0 + r) * 512);
+        load_lds16_async(vbase + base + off[r] + shift, vl + (slab0 + r) * 512);
+      } else {
         load_lds16(kbase + base + off[r] + shift, kl + (slab0 + r) * 512);
         load_lds16(vbase + base + off[r] + shift, vl + (slab0 + r) * 512);
       }
@@ -114,27 +119,48 @@ struct TileLoader {
   }
 };
 
+// Work unit of the 16-bit kernel. Non-causal: one query block. Causal: the
+// query blocks u and n-1-u of one (batch, head), one after the other, the
+// short one with keys in ascending tile order and the long one in descending
+// order. Every unit then streams the same number of key tiles, and at step g
+// all units of a head read either tile g or the one same tile counted from the
+// other end, so the concurrently running units of a head share their K/V
+// tiles in L2. The order of the key tiles does not change the result of the
+// online softmax (up to rounding).
+__device__ __forceinline__ int tile_count(int last_key) { return last_key >= 0 ? last_key / kBC + 1 : 0; }
+
+constexpr int kFwdStages = 2;   // LDS slots: tiles are loaded one step ahead
+
 template <class E, typename OutT, int D, bool CAUSAL, int NW>
 __global__ __launch_bounds__(NW * 64, 8 / NW)
 void fwd16_kernel(const FwdParams a) {
   constexpr int TILE = kBC * D;                 // elements per K or V tile
-  constexpr int CPR = D / 8;                    // 16-byte chunks per row
-  constexpr int SLABS = kBC * CPR / 64;         // 1 KiB wave-loads per tensor per tile
-  constexpr int SLABS_PER_WAVE = SLABS / NW;
   constexpr int QF = D / 16;
   constexpr int BR = NW * kQPW;
-  static_assert(SLABS_PER_WAVE * NW == SLABS, "tile must split evenly over the waves");
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2][2][TILE];   // [buffer][K, V]
+  constexpr int ST = kFwdStages;
+  constexpr int LPT = 2 * TileLoader<D, NW>::SPW;   // this wave's load instructions per tile
+  __shared__ __attribute__((aligned(16))) uint16_t smem[ST][2][TILE];   // [slot][K, V]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int L = xcd_remap(static_cast<int>(blockIdx.x), a.total);
-  const int bh = L / a.n_qblocks;
-  int qb = L - bh * a.n_qblocks;
-  if (CAUSAL) qb = a.n_qblocks - 1 - qb;   // longest causal rows first within each head
+  const int bh = L / a.units;
+  const int u = L - bh * a.units;
   const int b = bh / a.H, h = bh - b * a.H, hk = h / a.group;
-  const int q0 = qb * BR;
-  const int qw0 = q0 + wave * kQPW;
-  const int qrow = qw0 + (lane & 31);
+
+  const int qb_first = u;
+  const int qb_second = CAUSAL ? a.n_qblocks - 1 - u : u;
+  const int nseg = (CAUSAL && qb_second > qb_first) ? 2 : 1;
+  auto block_tiles = [&](int qb) {
+    int last = a.Nk - 1;
+    if (CAUSAL) last = min(last, qb * BR + BR - 1 + a.off);
+    return tile_count(last);
+  };
+  const int n0 = block_tiles(qb_first);
+  const int n1 = nseg == 2 ? block_tiles(qb_second) : 0;
+  const int n_steps = n0 + n1;
+  // Key tile streamed at step g: ascending through the first block, then
+  // descending through the second.
+  auto tile_at = [&](int g) { return g < n0 ? g : n_steps - 1 - g; };
 
   const int64_t q_rs = static_cast<int64_t>(a.H) * D;
   const int64_t kv_rs = static_cast<int64_t>(a.Hkv) * D;
@@ -142,28 +168,6 @@ void fwd16_kernel(const FwdParams a) {
                           static_cast<int64_t>(b) * a.Nk * kv_rs + static_cast<int64_t>(hk) * D;
   const uint16_t* vbase = static_cast<const uint16_t*>(a.v) +
                           static_cast<int64_t>(b) * a.Nk * kv_rs + static_cast<int64_t>(hk) * D;
-
-  // Q^T operand: lane l holds Q[row][16c + 8(l/32) .. +8].
-  typename E::vec8 qf[QF];
-  {
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
-                         (static_cast<int64_t>(b) * a.Nq + qrow) * q_rs +
-                         static_cast<int64_t>(h) * D + 8 * (lane >> 5);
-#pragma unroll
-    for (int c = 0; c < QF; ++c) {
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (qrow < a.Nq) u = *reinterpret_cast<const uint4*>(qp + 16 * c);
-      qf[c] = __builtin_bit_cast(typename E::vec8, u);
-    }
-  }
-
-  int last_key = a.Nk - 1;
-  int wave_last = a.Nk - 1;
-  if (CAUSAL) {
-    last_key = min(last_key, q0 + BR - 1 + a.off);
-    wave_last = min(wave_last, qw0 + kQPW - 1 + a.off);
-  }
-  const int n_tiles = last_key >= 0 ? last_key / kBC + 1 : 0;
 
   // Per-lane LDS read geometry.
   const int kr = lane & 31;                 // K operand row within a 32-key block
@@ -175,132 +179,178 @@ void fwd16_kernel(const FwdParams a) {
   const int vcl = 2 * (blk & 1) + ((r16 & 3) >> 1);      // chunk within a 32-wide d block
   const int vin = (r16 & 1) * 4;                          // element within the chunk
 
-  f32x16 acc[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
-  float m_run = kNegInf, m2_run = kNegInf, l_run = 0.f;   // this lane's query row
-
   const TileLoader<D, NW> loader(kv_rs, wave, lane);
-  if (n_tiles > 0) loader.load(kbase, vbase, kv_rs, 0, a.Nk, &smem[0][0][0], &smem[0][1][0]);
-  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-
-  for (int j = 0; j < n_tiles; ++j) {
-    const int k0 = j * kBC;
-    const int buf = j & 1;
-    if (j + 1 < n_tiles)
-      loader.load(kbase, vbase, kv_rs, k0 + kBC, a.Nk, &smem[buf ^ 1][0][0], &smem[buf ^ 1][1][0]);
-    if (k0 <= wave_last) {
-      const uint16_t* kl = &smem[buf][0][0];
-      const uint16_t* vl = &smem[buf][1][0];
-      // S^T = K Q^T: the two 32-key chains interleave and the K operands of
-      // step c+1 are read from LDS while step c multiplies.
-      f32x16 s[2] = {f32x16{}, f32x16{}};
-      {
-        const uint16_t* row0 = kl + kr * D;
-        const uint16_t* row1 = row0 + 32 * D;
-        using V8 = typename E::vec8;
-        V8 a0 = *reinterpret_cast<const V8*>(row0 + ((khi ^ ksw) * 8));
-        V8 a1 = *reinterpret_cast<const V8*>(row1 + ((khi ^ ksw) * 8));
 #pragma unroll
-        for (int c = 0; c < QF; ++c) {
-          V8 n0 = a0, n1 = a1;
-          if (c + 1 < QF) {
-            n0 = *reinterpret_cast<const V8*>(row0 + (((2 * c + 2 + khi) ^ ksw) * 8));
-            n1 = *reinterpret_cast<const V8*>(row1 + (((2 * c + 2 + khi) ^ ksw) * 8));
-          }
-          s[0] = E::mma32(a0, qf[c], s[0]);
-          s[1] = E::mma32(a1, qf[c], s[1]);
-          a0 = n0;
-          a1 = n1;
-        }
-      }
+  for (int t = 0; t < ST - 1; ++t)
+    if (t < n_steps)
+      loader.template load<true>(kbase, vbase, kv_rs, tile_at(t) * kBC, a.Nk, &smem[t][0][0],
+                                 &smem[t][1][0]);
 
-      const bool need_mask = (k0 + kBC > a.Nk) || (CAUSAL && k0 + kBC - 1 > qw0 + a.off);
-      if (need_mask) {
-        const int lim = CAUSAL ? min(a.Nk - 1, qrow + a.off) : a.Nk - 1;
+  int g = 0;                   // step counter over both blocks
+  int buf = 0;                 // slot of the tile of step g
+  int nbuf = ST - 1;           // slot that the tile of step g + ST - 1 loads into
+  for (int seg = 0; seg < nseg; ++seg) {
+    const int qb = seg == 0 ? qb_first : qb_second;
+    const int nt = seg == 0 ? n0 : n1;
+    const int q0 = qb * BR;
+    const int qw0 = q0 + wave * kQPW;
+    const int qrow = qw0 + (lane & 31);
+    const int wave_last = CAUSAL ? min(a.Nk - 1, qw0 + kQPW - 1 + a.off) : a.Nk - 1;
+
+    // Q^T operand: lane l holds Q[row][16c + 8(l/32) .. +8].
+    typename E::vec8 qf[QF];
+    {
+      const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
+                           (static_cast<int64_t>(b) * a.Nq + qrow) * q_rs +
+                           static_cast<int64_t>(h) * D + 8 * (lane >> 5);
+#pragma unroll
+      for (int c = 0; c < QF; ++c) {
+        uint4 v4 = make_uint4(0, 0, 0, 0);
+        if (qrow < a.Nq) v4 = *reinterpret_cast<const uint4*>(qp + 16 * c);
+        qf[c] = __builtin_bit_cast(typename E::vec8, v4);
+      }
+    }
+    // Consuming the fragments here makes the compiler wait for their loads
+    // once, instead of at every score product of the loop.
+#pragma unroll
+    for (int c = 0; c < QF; ++c) __asm__ volatile("" : "+v"(qf[c]));
+    if (seg == 0)
+      __asm__ volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+    f32x16 acc[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
+    float m_run = kNegInf, m2_run = kNegInf, l_run = 0.f;   // this lane's query row
+
+    for (int j = 0; j < nt; ++j, ++g) {
+      const int k0 = (seg == 0 ? j : nt - 1 - j) * kBC;
+      const bool more = g + ST - 1 < n_steps;
+      if (more)
+        loader.template load<true>(kbase, vbase, kv_rs, tile_at(g + ST - 1) * kBC, a.Nk,
+                                   &smem[nbuf][0][0], &smem[nbuf][1][0]);
+      if (k0 <= wave_last) {
+        const uint16_t* kl = &smem[buf][0][0];
+        const uint16_t* vl = &smem[buf][1][0];
+        // S^T = K Q^T: the two 32-key chains interleave and the K operands of
+        // step c+1 are read from LDS while step c multiplies.
+        f32x16 s[2] = {f32x16{}, f32x16{}};
+        {
+          const uint16_t* row0 = kl + kr * D;
+          const uint16_t* row1 = row0 + 32 * D;
+          using V8 = typename E::vec8;
+          V8 a0 = *reinterpret_cast<const V8*>(row0 + ((khi ^ ksw) * 8));
+          V8 a1 = *reinterpret_cast<const V8*>(row1 + ((khi ^ ksw) * 8));
+#pragma unroll
+          for (int c = 0; c < QF; ++c) {
+            V8 n0v = a0, n1v = a1;
+            if (c + 1 < QF) {
+              n0v = *reinterpret_cast<const V8*>(row0 + (((2 * c + 2 + khi) ^ ksw) * 8));
+              n1v = *reinterpret_cast<const V8*>(row1 + (((2 * c + 2 + khi) ^ ksw) * 8));
+            }
+            s[0] = E::mma32(a0, qf[c], s[0]);
+            s[1] = E::mma32(a1, qf[c], s[1]);
+            a0 = n0v;
+            a1 = n1v;
+          }
+        }
+
+        const bool need_mask = (k0 + kBC > a.Nk) || (CAUSAL && k0 + kBC - 1 > qw0 + a.off);
+        if (need_mask) {
+          const int lim = CAUSAL ? min(a.Nk - 1, qrow + a.off) : a.Nk - 1;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int key = k0 + 32 * kb + 8 * (i >> 2) + 4 * khi + (i & 3);
+              if (key > lim) s[kb][i] = kNegInf;
+            }
+        }
+
+        float mx = kNegInf;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+        mx = max_xor32(mx);
+        // Exact running max: the largest probability of the row is exactly 1,
+        // so it passes the rounding of P to the input type unchanged. A row
+        // whose keys in this tile are all masked keeps m = -inf, p = 0.
+        const float m_new = fmaxf(m_run, mx);
+        const float m2_new = m_new * a.c;
+        const float m2_use = (m_new == kNegInf) ? 0.f : m2_new;
+        const float alpha = (m_new == m_run) ? 1.f : exp2_fast(m2_run - m2_new);
+        if (__any(alpha != 1.f)) {
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+        }
+        float rs = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int key = k0 + 32 * kb + 8 * (i >> 2) + 4 * khi + (i & 3);
-            if (key > lim) s[kb][i] = kNegInf;
+            const float p = exp2_fast(fmaf(s[kb][i], a.c, -m2_use));
+            s[kb][i] = p;
+            rs += p;
           }
-      }
+        l_run = fmaf(alpha, l_run, rs);
+        m_run = m_new;
+        m2_run = m2_new;
 
-      float mx = kNegInf;
+        // O^T += V^T P^T, keys in the order the score layout holds them.
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-      mx = max_xor32(mx);
-      // Exact running max: the largest probability of the row is exactly 1,
-      // so it passes the rounding of P to the input type unchanged.
-      const float m_new = fmaxf(m_run, mx);
-      const float m2_new = m_new * a.c;
-      const float m2_use = (m_new == kNegInf) ? 0.f : m2_new;
-      const float alpha = (m_new == m_run) ? 1.f : exp2_fast(m2_run - m2_new);
-      if (__any(alpha != 1.f)) {
+          for (int hh = 0; hh < 2; ++hh) {
+            const int o = 8 * hh;
+            const auto bop = pack8<E>(s[kb][o + 0], s[kb][o + 1], s[kb][o + 2], s[kb][o + 3],
+                                      s[kb][o + 4], s[kb][o + 5], s[kb][o + 6], s[kb][o + 7]);
+            const uint16_t* r0 = vl + (32 * kb + 16 * hh + vrow) * D + vin;
+            const uint16_t* r1 = r0 + 8 * D;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
-      }
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = exp2_fast(fmaf(s[kb][i], a.c, -m2_use));
-          s[kb][i] = p;
-          rs += p;
-        }
-      l_run = fmaf(alpha, l_run, rs);
-      m_run = m_new;
-      m2_run = m2_new;
-
-      // O^T += V^T P^T, keys in the order the score layout holds them.
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int o = 8 * hh;
-          const auto bop = pack8<E>(s[kb][o + 0], s[kb][o + 1], s[kb][o + 2], s[kb][o + 3],
-                                    s[kb][o + 4], s[kb][o + 5], s[kb][o + 6], s[kb][o + 7]);
-          const uint16_t* r0 = vl + (32 * kb + 16 * hh + vrow) * D + vin;
-          const uint16_t* r1 = r0 + 8 * D;
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db) {
-            const int ch = 4 * db + vcl;
-            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) i16x4*)(r0 + ((ch ^ vsw0) * 8)));
-            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) i16x4*)(r1 + ((ch ^ vsw1) * 8)));
-            typedef short i16x8 __attribute__((ext_vector_type(8)));
-            const i16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            acc[db] = E::mma32(__builtin_bit_cast(typename E::vec8, w), bop, acc[db]);
+            for (int db = 0; db < D / 32; ++db) {
+              const int ch = 4 * db + vcl;
+              const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (__attribute__((address_space(3))) i16x4*)(r0 + ((ch ^ vsw0) * 8)));
+              const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (__attribute__((address_space(3))) i16x4*)(r1 + ((ch ^ vsw1) * 8)));
+              typedef short i16x8 __attribute__((ext_vector_type(8)));
+              const i16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+              acc[db] = E::mma32(__builtin_bit_cast(typename E::vec8, w), bop, acc[db]);
+            }
           }
         }
       }
+      // The tile of step g+1 must be resident before the next step; younger
+      // tiles may still be in flight. Each wave waits for its own loads
+      // (issued from inline assembly, so the compiler does not track them),
+      // then all waves meet.
+      if (ST > 2 && more) {
+        __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"((ST > 2 ? ST - 2 : 0) * LPT) : "memory");
+      } else {
+        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      buf = (buf + 1 == ST) ? 0 : buf + 1;
+      nbuf = (nbuf + 1 == ST) ? 0 : nbuf + 1;
     }
-    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-  }
 
-  const float l_tot = sum_xor32(l_run);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (qrow < a.Nq) {
-    OutT* orow = static_cast<OutT*>(a.o) + (static_cast<int64_t>(b) * a.Nq + qrow) * q_rs +
-                 static_cast<int64_t>(h) * D;
+    const float l_tot = sum_xor32(l_run);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (qrow < a.Nq) {
+      OutT* orow = static_cast<OutT*>(a.o) + (static_cast<int64_t>(b) * a.Nq + qrow) * q_rs +
+                   static_cast<int64_t>(h) * D;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+      for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        store4(orow + 32 * db + 8 * g + 4 * khi, acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv,
-               acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv);
-    if (lane < 32)
-      a.lse[(static_cast<int64_t>(b) * a.H + h) * a.Nq + qrow] =
-          l_tot > 0.f ? (m2_run + log2f(l_tot)) * kLn2 : kNegInf;
+        for (int gg = 0; gg < 4; ++gg)
+          store4(orow + 32 * db + 8 * gg + 4 * khi, acc[db][4 * gg] * inv,
+                 acc[db][4 * gg + 1] * inv, acc[db][4 * gg + 2] * inv, acc[db][4 * gg + 3] * inv);
+      if (lane < 32)
+        a.lse[(static_cast<int64_t>(b) * a.H + h) * a.Nq + qrow] =
+            l_tot > 0.f ? (m2_run + log2f(l_tot)) * kLn2 : kNegInf;
+    }
   }
 }
 
@@ -524,7 +574,7 @@ hipError_t launch_t(const FwdParams& p, bool causal, hipStream_t s) {
   return hipGetLastError();
 }
 
-constexpr int kNW16 = 4;   // waves per workgroup of the 16-bit kernel
+constexpr int kNW16 = 8;   // waves per workgroup of the 16-bit kernel (2 per SIMD)
 
 template <class E, typename OutT, int D>
 hipError_t launch16(const FwdParams& p, bool causal, hipStream_t s) {
@@ -560,9 +610,12 @@ hipError_t launch_forward(const ForwardArgs& a, hipStream_t s) {
   p.q = a.q; p.k = a.k; p.v = a.v; p.o = a.o; p.lse = a.lse;
   p.B = a.B; p.H = a.H; p.Hkv = a.Hkv; p.Nq = a.Nq; p.Nk = a.Nk;
   p.group = a.H / a.Hkv;
-  const int br = a.in_dtype == FA_F32 ? kBR : kNW16 * kQPW;
+  const bool f32 = a.in_dtype == FA_F32;
+  const int br = f32 ? kBR : kNW16 * kQPW;
   p.n_qblocks = (a.Nq + br - 1) / br;
-  p.total = a.B * a.H * p.n_qblocks;
+  // 16-bit causal: query blocks u and n-1-u share one workgroup.
+  p.units = (!f32 && a.causal) ? (p.n_qblocks + 1) / 2 : p.n_qblocks;
+  p.total = a.B * a.H * p.units;
   p.c = a.scale * kLog2e;
   p.off = a.Nk - a.Nq;
   if (p.total == 0) return hipSuccess;
