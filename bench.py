@@ -103,6 +103,97 @@ def cpu_baseline_decode(pi, d, target_s):
                        f"{dt:.1f} s")
 
 
+def time_steps(torch, fn, n):
+    """Mean ms per call of n back-to-back calls on the current stream."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def bench_decode_variants(torch, fa, inputs, pi, dev, lens, dp, steps):
+    """The decode with a 4096-token window and logit cap 50: GB/s of the KV
+    bytes the window leaves visible."""
+    import numpy as np
+    window, cap = 4096, 50.0
+    vis = np.minimum(lens, window).astype(np.float64)
+    kv = float(vis.sum()) * dp["Hkv"] * dp["d"] * 2 * 2
+    ws = torch.empty(fa.decode_workspace_size(dp["B"], dp["H"], dp["d"], fa.MAX_SPLITS),
+                     dtype=torch.uint8, device="cuda")
+    od = torch.empty_like(dev["q"])
+    ld = torch.empty((dp["B"], dp["H"]), dtype=torch.float32, device="cuda")
+
+    def run():
+        fa.decode_paged_ex(dev["q"], dev["k"], dev["v"], dev["t"], dev["s"], window=window,
+                           softcap=cap, out=od, lse=ld, workspace=ws)
+    for _ in range(3):
+        run()
+    ms = time_steps(torch, run, max(steps, 10))
+    return {"workload": DECODE + " window=4096 softcap=50", "ms_mean": ms,
+            "visible_kv_bytes": kv, "value": kv / (ms * 1e-3) / 1e9, "unit": "GB/s",
+            "frac_hbm": kv / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+
+
+def bench_decode_graph(torch, fa, inputs, dev, dp, n=200):
+    """Launch overhead: eager decode step (decode + merge launches) against one
+    graph replay, on the paged-decode workload and on a one-sequence step."""
+    import numpy as np
+    out = {}
+    small_lens = np.array([1024], dtype=np.int64)
+    spi = inputs.paged_decode_inputs(1, dp["H"], dp["Hkv"], dp["d"], small_lens, seed=7)
+    sdev = dict(q=spi.q.cuda(), k=spi.k_pool.cuda(), v=spi.v_pool.cuda(),
+                t=spi.block_table.cuda(), s=spi.seq_lens.cuda())
+    for name, d in (("b64_h32_kv8_paged", dev), ("b1_len1024", sdev)):
+        B, H, hd = d["q"].shape
+        ws = torch.empty(fa.decode_workspace_size(B, H, hd, fa.MAX_SPLITS), dtype=torch.uint8,
+                         device="cuda")
+        o = torch.empty_like(d["q"])
+        lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+        g = fa.DecodeGraph(d["q"], d["k"], d["v"], d["t"], d["s"], out=o, lse=lse, workspace=ws)
+
+        def eager():
+            fa.decode_paged(d["q"], d["k"], d["v"], d["t"], d["s"], out=o, lse=lse, workspace=ws)
+        for _ in range(3):
+            eager()
+            g.launch()
+        torch.cuda.synchronize()
+        t_e = time_steps(torch, eager, n)
+        t_g = time_steps(torch, g.launch, n)
+        g.close()
+        out[name] = {"eager_us_per_step": t_e * 1e3, "graph_us_per_step": t_g * 1e3,
+                     "saved_us_per_step": (t_e - t_g) * 1e3, "steps": n}
+        if name == "b1_len1024":
+            # a model step: one decode per layer, 32 layers, replayed as one graph
+            layers = 32
+            cg = torch.cuda.CUDAGraph()
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                for _ in range(3):
+                    eager()
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(cg):
+                for _ in range(layers):
+                    eager()
+            torch.cuda.synchronize()
+
+            def many():
+                for _ in range(layers):
+                    eager()
+            reps = max(1, n // layers)
+            t_me = time_steps(torch, many, reps)
+            t_mg = time_steps(torch, cg.replay, reps)
+            out["b1_len1024_x32_layers"] = {"eager_us_per_step": t_me * 1e3,
+                                            "graph_us_per_step": t_mg * 1e3,
+                                            "saved_us_per_step": (t_me - t_mg) * 1e3,
+                                            "steps": reps, "layers": layers}
+    return out
+
+
 def copy_calibration(torch, nbytes=1 << 30, reps=5):
     """A plain device copy of known size, for scaling HBM byte counters."""
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
@@ -120,8 +211,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--parts", default="prefill,decode",
-                    help="comma list of the step's parts to run (profiling aid)")
+    ap.add_argument("--parts", default="prefill,decode,variants,graph",
+                    help="comma list: prefill, decode (the timed step), variants (windowed "
+                         "and soft-capped decode), graph (graph-replayed decode step)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of each oracle baseline sample (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -162,12 +254,13 @@ def main():
 
     lens = inputs.uniform_lengths(dp["B"], dp["len_lo"], dp["len_hi"], dp["seed"])
     kv_bytes = float(lens.sum()) * dp["Hkv"] * dp["d"] * 2 * 2
-    if "decode" in parts or args.cpu_seconds > 0:
+    need_decode = bool(parts & {"decode", "variants", "graph"})
+    if need_decode or args.cpu_seconds > 0:
         log(f"bench: generating {DECODE} inputs")
         pi = inputs.paged_decode_inputs(dp["B"], dp["H"], dp["Hkv"], dp["d"], lens, dp["seed"],
                                         pool_factor=dp["pool_factor"],
                                         max_pages=dp["len_hi"] // 16)
-    if "decode" in parts:
+    if need_decode:
         dq, dk, dv = pi.q.to(dev), pi.k_pool.to(dev), pi.v_pool.to(dev)
         dt_, ds_ = pi.block_table.to(dev), pi.seq_lens.to(dev)
         od = torch.empty_like(dq)
@@ -204,6 +297,17 @@ def main():
     dec_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
     log(f"bench: prefill ms mean {pre_ms.mean():.3f} min {pre_ms.min():.3f}; "
         f"decode ms mean {dec_ms.mean():.3f} min {dec_ms.min():.3f}")
+
+    next_rows = {}
+    if need_decode:
+        ddev = dict(q=dq, k=dk, v=dv, t=dt_, s=ds_)
+        if "variants" in parts:
+            log("bench: windowed / soft-capped decode")
+            next_rows["decode_window_softcap"] = bench_decode_variants(
+                torch, fa, inputs, pi, ddev, lens, dp, args.steps)
+        if "graph" in parts:
+            log("bench: graph-replayed decode step")
+            next_rows["decode_graph"] = bench_decode_graph(torch, fa, inputs, ddev, dp)
 
     pre_tflops = flops / (pre_ms.mean() * 1e-3) / 1e12 if "prefill" in parts else None
     dec_gbps = kv_bytes / (dec_ms.mean() * 1e-3) / 1e9 if "decode" in parts else None
@@ -250,6 +354,7 @@ def main():
             "traffic_detail": tr_dec},
         "cpu_baseline": cpu,
         "cpu_baseline_decode": cpu_dec,
+        "next_rows": next_rows or None,
     }
     print(json.dumps(line))
 

@@ -37,6 +37,13 @@ _SIGNATURES = {
     "fa_decode_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "fa_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I,
                              _I, _I, _P, ctypes.c_size_t, _P]),
+    "fa_decode_paged_ex": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F,
+                                _I, _I, _F, _I, _I, _P, ctypes.c_size_t, _P]),
+    "fa_decode_graph_create": (_I, [ctypes.POINTER(ctypes.c_void_p), _P, _P, _P, _P, _P, _P,
+                                    _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _F, _I, _I, _P,
+                                    ctypes.c_size_t]),
+    "fa_decode_graph_launch": (_I, [_P, _P]),
+    "fa_decode_graph_destroy": (None, [_P]),
     "fa_merge_partials": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "fa_status_string": (ctypes.c_char_p, [_I]),
     "fa_version": (ctypes.c_char_p, []),
@@ -133,10 +140,8 @@ def decode_workspace_size(B: int, H: int, d: int, max_splits: int) -> int:
     return int(lib().fa_decode_workspace_size(B, H, d, max_splits))
 
 
-def decode_paged(q, k_pool, v_pool, block_table, seq_lens, scale: float | None = None,
-                 num_splits: int = 0, out_dtype=None, out=None, lse=None, workspace=None):
-    """Paged decode. q [B,H,d]; pools [P,16,Hkv,d]; block_table [B,max_pages] int32;
-    seq_lens [B] int32 -> (O [B,H,d], LSE [B,H])."""
+def _decode(entry, q, k_pool, v_pool, block_table, seq_lens, scale, num_splits, out_dtype, out,
+            lse, workspace, extra):
     if q.dim() != 3 or k_pool.dim() != 4 or v_pool.shape != k_pool.shape:
         raise ValueError("expected q [B,H,d] and pools [P,page,Hkv,d]")
     B, H, d = q.shape
@@ -155,14 +160,93 @@ def decode_paged(q, k_pool, v_pool, block_table, seq_lens, scale: float | None =
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = lib().fa_decode_paged(
-        _dev(q, "q"), _dev(k_pool, "k_pool", q.dtype), _dev(v_pool, "v_pool", q.dtype),
-        _dev(block_table, "block_table", torch.int32), _dev(seq_lens, "seq_lens", torch.int32),
-        _dev(out, "out", out_dtype), _dev(lse, "lse", torch.float32),
-        B, H, Hkv, d, page, block_table.shape[1], num_pages, scale, int(num_splits),
-        _code(q.dtype), _code(out_dtype), ws_ptr, ws_bytes, _stream(q.device))
-    _check(st, "fa_decode_paged")
+    fn = getattr(lib(), entry)
+    st = fn(_dev(q, "q"), _dev(k_pool, "k_pool", q.dtype), _dev(v_pool, "v_pool", q.dtype),
+            _dev(block_table, "block_table", torch.int32), _dev(seq_lens, "seq_lens", torch.int32),
+            _dev(out, "out", out_dtype), _dev(lse, "lse", torch.float32),
+            B, H, Hkv, d, page, block_table.shape[1], num_pages, scale, int(num_splits), *extra,
+            _code(q.dtype), _code(out_dtype), ws_ptr, ws_bytes, _stream(q.device))
+    _check(st, entry)
     return out, lse
+
+
+def decode_paged(q, k_pool, v_pool, block_table, seq_lens, scale: float | None = None,
+                 num_splits: int = 0, out_dtype=None, out=None, lse=None, workspace=None):
+    """Paged decode. q [B,H,d]; pools [P,16,Hkv,d]; block_table [B,max_pages] int32;
+    seq_lens [B] int32 -> (O [B,H,d], LSE [B,H])."""
+    return _decode("fa_decode_paged", q, k_pool, v_pool, block_table, seq_lens, scale,
+                   num_splits, out_dtype, out, lse, workspace, ())
+
+
+def decode_paged_ex(q, k_pool, v_pool, block_table, seq_lens, window: int = 0,
+                    softcap: float = 0.0, scale: float | None = None, num_splits: int = 0,
+                    out_dtype=None, out=None, lse=None, workspace=None):
+    """Paged decode with a sliding window (newest `window` tokens visible, 0 = all) and
+    logit soft-capping (scaled scores x -> softcap*tanh(x/softcap), 0 = off)."""
+    return _decode("fa_decode_paged_ex", q, k_pool, v_pool, block_table, seq_lens, scale,
+                   num_splits, out_dtype, out, lse, workspace, (int(window), float(softcap)))
+
+
+class DecodeGraph:
+    """A paged decode step recorded once as a HIP graph (fa_decode_graph_*).
+
+    The graph binds the tensors given at construction; write each step's inputs
+    into them (q, the caches, block_table, seq_lens) and call `launch()`; the
+    results land in `out` and `lse`. Keep every tensor alive and unmoved while
+    the graph exists.
+    """
+
+    def __init__(self, q, k_pool, v_pool, block_table, seq_lens, window: int = 0,
+                 softcap: float = 0.0, scale: float | None = None, num_splits: int = 0,
+                 out_dtype=None, out=None, lse=None, workspace=None):
+        if q.dim() != 3 or k_pool.dim() != 4 or v_pool.shape != k_pool.shape:
+            raise ValueError("expected q [B,H,d] and pools [P,page,Hkv,d]")
+        B, H, d = q.shape
+        num_pages, page, Hkv = k_pool.shape[0], k_pool.shape[1], k_pool.shape[2]
+        if block_table.dim() != 2 or block_table.shape[0] != B or tuple(seq_lens.shape) != (B,):
+            raise ValueError("block_table must be [B, max_pages] and seq_lens [B]")
+        out_dtype = q.dtype if out_dtype is None else out_dtype
+        self.out = out if out is not None else torch.empty((B, H, d), dtype=out_dtype,
+                                                           device=q.device)
+        self.lse = lse if lse is not None else torch.empty((B, H), dtype=torch.float32,
+                                                           device=q.device)
+        S = num_splits if num_splits > 0 else MAX_SPLITS
+        need = decode_workspace_size(B, H, d, S) if B > 0 else 0
+        if workspace is None and S > 1 and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        self.workspace = workspace
+        # the graph holds raw pointers: keep the tensors referenced
+        self._keep = (q, k_pool, v_pool, block_table, seq_lens)
+        self.device = q.device
+        scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+        ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        handle = ctypes.c_void_p()
+        st = lib().fa_decode_graph_create(
+            ctypes.byref(handle), _dev(q, "q"), _dev(k_pool, "k_pool", q.dtype),
+            _dev(v_pool, "v_pool", q.dtype), _dev(block_table, "block_table", torch.int32),
+            _dev(seq_lens, "seq_lens", torch.int32), _dev(self.out, "out", out_dtype),
+            _dev(self.lse, "lse", torch.float32), B, H, Hkv, d, page, block_table.shape[1],
+            num_pages, scale, int(num_splits), int(window), float(softcap), _code(q.dtype),
+            _code(out_dtype), ws_ptr, ws_bytes)
+        _check(st, "fa_decode_graph_create")
+        self._handle = handle
+
+    def launch(self, stream=None):
+        s = _stream(self.device) if stream is None else stream.cuda_stream
+        _check(lib().fa_decode_graph_launch(self._handle, s), "fa_decode_graph_launch")
+        return self.out, self.lse
+
+    def close(self):
+        if getattr(self, "_handle", None) is not None and self._handle.value:
+            lib().fa_decode_graph_destroy(self._handle)
+            self._handle = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # interpreter shutdown
+            pass
 
 
 def merge_partials(o_parts, lse_parts, num_parts=None, out_dtype=torch.float32, out=None,

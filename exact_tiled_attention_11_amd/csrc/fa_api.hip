@@ -4,6 +4,7 @@
 // no side effect at all.
 #include <cmath>
 #include <cstdint>
+#include <new>
 
 #include "fa.h"
 #include "fa_internal.hpp"
@@ -75,18 +76,26 @@ size_t fa_decode_workspace_size(int B, int H, int d, int max_splits) {
   return o_bytes + rows * sizeof(float);
 }
 
-fa_status fa_decode_paged(const void* q, const void* K_pool, const void* V_pool,
-                          const int32_t* block_table, const int32_t* seq_lens, void* O, float* LSE,
-                          int B, int H, int Hkv, int d, int page_size, int max_pages_per_seq,
-                          int num_pages, float scale, int num_splits, fa_dtype dtype,
-                          fa_dtype out_dtype, void* workspace, size_t workspace_bytes,
-                          void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validates a decode call and fills `a`; launches nothing. `*empty` is set
+// when the call is valid but has no work (B == 0).
+fa_status decode_prepare(const void* q, const void* K_pool, const void* V_pool,
+                         const int32_t* block_table, const int32_t* seq_lens, void* O, float* LSE,
+                         int B, int H, int Hkv, int d, int page_size, int max_pages_per_seq,
+                         int num_pages, float scale, int num_splits, int window, float softcap,
+                         fa_dtype dtype, fa_dtype out_dtype, void* workspace,
+                         size_t workspace_bytes, fa::DecodeArgs* out, bool* empty) {
+  *empty = false;
   if (B < 0 || H < 1 || Hkv < 1 || H % Hkv != 0 || max_pages_per_seq < 1 || num_pages < 1 ||
       page_size < 1)
     return FA_ERR_BAD_SHAPE;
   if (num_splits < 0 || num_splits > FA_MAX_SPLITS) return FA_ERR_BAD_ARG;
   if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return FA_ERR_BAD_ARG;
   if (!scale_ok(scale)) return FA_ERR_BAD_ARG;
+  if (window < 0 || !std::isfinite(softcap) || softcap < 0.f) return FA_ERR_BAD_ARG;
   const int G = H / Hkv;
   if (!head_dim_ok(d) || page_size != FA_PAGE_SIZE || dtype == FA_F32 ||
       !(G == 1 || G == 2 || G == 4 || G == 8))
@@ -96,7 +105,10 @@ fa_status fa_decode_paged(const void* q, const void* K_pool, const void* V_pool,
       int64_t{B} * max_pages_per_seq > kMaxElems || int64_t{B} * H * d > kMaxElems ||
       int64_t{max_pages_per_seq} * page_size > kMaxElems || B > 65535 || Hkv > 65535)
     return FA_ERR_BAD_SHAPE;
-  if (B == 0) return FA_OK;
+  if (B == 0) {
+    *empty = true;
+    return FA_OK;
+  }
   if (!q || !K_pool || !V_pool || !block_table || !seq_lens || !O || !LSE)
     return FA_ERR_NULL_PTR;
   if (!aligned16(q) || !aligned16(K_pool) || !aligned16(V_pool)) return FA_ERR_BAD_ARG;
@@ -110,6 +122,7 @@ fa_status fa_decode_paged(const void* q, const void* K_pool, const void* V_pool,
   a.B = B; a.H = H; a.Hkv = Hkv; a.d = d; a.page_size = page_size;
   a.max_pages = max_pages_per_seq; a.num_pages = num_pages;
   a.scale = scale; a.num_splits = num_splits;
+  a.window = window; a.softcap = softcap;
   a.dtype = dtype; a.out_dtype = out_dtype;
   a.max_splits = S;
   const size_t rows = static_cast<size_t>(B) * H * S;
@@ -117,7 +130,110 @@ fa_status fa_decode_paged(const void* q, const void* K_pool, const void* V_pool,
   a.part_lse = workspace ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                                     (rows * d * sizeof(float) + 255) / 256 * 256)
                          : nullptr;
+  *out = a;
+  return FA_OK;
+}
+
+fa_status decode_impl(const void* q, const void* K_pool, const void* V_pool,
+                      const int32_t* block_table, const int32_t* seq_lens, void* O, float* LSE,
+                      int B, int H, int Hkv, int d, int page_size, int max_pages_per_seq,
+                      int num_pages, float scale, int num_splits, int window, float softcap,
+                      fa_dtype dtype, fa_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  fa::DecodeArgs a;
+  bool empty;
+  const fa_status st = decode_prepare(q, K_pool, V_pool, block_table, seq_lens, O, LSE, B, H,
+                                      Hkv, d, page_size, max_pages_per_seq, num_pages, scale,
+                                      num_splits, window, softcap, dtype, out_dtype, workspace,
+                                      workspace_bytes, &a, &empty);
+  if (st != FA_OK || empty) return st;
   return from_hip(fa::launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_decode_paged(const void* q, const void* K_pool, const void* V_pool,
+                          const int32_t* block_table, const int32_t* seq_lens, void* O, float* LSE,
+                          int B, int H, int Hkv, int d, int page_size, int max_pages_per_seq,
+                          int num_pages, float scale, int num_splits, fa_dtype dtype,
+                          fa_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  return decode_impl(q, K_pool, V_pool, block_table, seq_lens, O, LSE, B, H, Hkv, d, page_size,
+                     max_pages_per_seq, num_pages, scale, num_splits, 0, 0.f, dtype, out_dtype,
+                     workspace, workspace_bytes, stream);
+}
+
+fa_status fa_decode_paged_ex(const void* q, const void* K_pool, const void* V_pool,
+                             const int32_t* block_table, const int32_t* seq_lens, void* O,
+                             float* LSE, int B, int H, int Hkv, int d, int page_size,
+                             int max_pages_per_seq, int num_pages, float scale, int num_splits,
+                             int window, float softcap, fa_dtype dtype, fa_dtype out_dtype,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(q, K_pool, V_pool, block_table, seq_lens, O, LSE, B, H, Hkv, d, page_size,
+                     max_pages_per_seq, num_pages, scale, num_splits, window, softcap, dtype,
+                     out_dtype, workspace, workspace_bytes, stream);
+}
+
+struct fa_decode_graph {
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+};
+
+fa_status fa_decode_graph_create(fa_decode_graph** out, const void* q, const void* K_pool,
+                                 const void* V_pool, const int32_t* block_table,
+                                 const int32_t* seq_lens, void* O, float* LSE, int B, int H,
+                                 int Hkv, int d, int page_size, int max_pages_per_seq,
+                                 int num_pages, float scale, int num_splits, int window,
+                                 float softcap, fa_dtype dtype, fa_dtype out_dtype,
+                                 void* workspace, size_t workspace_bytes) {
+  if (!out) return FA_ERR_NULL_PTR;
+  *out = nullptr;
+  fa::DecodeArgs a;
+  bool empty;
+  const fa_status st = decode_prepare(q, K_pool, V_pool, block_table, seq_lens, O, LSE, B, H,
+                                      Hkv, d, page_size, max_pages_per_seq, num_pages, scale,
+                                      num_splits, window, softcap, dtype, out_dtype, workspace,
+                                      workspace_bytes, &a, &empty);
+  if (st != FA_OK) return st;
+  hipStream_t cs;
+  if (hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) != hipSuccess) return FA_ERR_HIP;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  bool ok = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) == hipSuccess;
+  if (ok) {
+    const hipError_t le = empty ? hipSuccess : fa::launch_decode(a, cs);
+    const hipError_t ce = hipStreamEndCapture(cs, &graph);
+    ok = le == hipSuccess && ce == hipSuccess && graph != nullptr;
+  }
+  if (ok) ok = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0) == hipSuccess;
+  (void)hipStreamDestroy(cs);
+  if (!ok) {
+    if (exec) (void)hipGraphExecDestroy(exec);
+    if (graph) (void)hipGraphDestroy(graph);
+    return FA_ERR_HIP;
+  }
+  fa_decode_graph* g = new (std::nothrow) fa_decode_graph{graph, exec};
+  if (!g) {
+    (void)hipGraphExecDestroy(exec);
+    (void)hipGraphDestroy(graph);
+    return FA_ERR_HIP;
+  }
+  *out = g;
+  return FA_OK;
+}
+
+fa_status fa_decode_graph_launch(const fa_decode_graph* g, void* stream) {
+  if (!g) return FA_ERR_NULL_PTR;
+  return from_hip(hipGraphLaunch(g->exec, static_cast<hipStream_t>(stream)));
+}
+
+void fa_decode_graph_destroy(fa_decode_graph* g) {
+  if (!g) return;
+  (void)hipGraphExecDestroy(g->exec);
+  (void)hipGraphDestroy(g->graph);
+  delete g;
 }
 
 fa_status fa_merge_partials(const float* o_parts, const float* lse_parts, const int32_t* num_parts,

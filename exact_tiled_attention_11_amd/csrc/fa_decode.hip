@@ -27,6 +27,10 @@
 //   * finally the 4 wave states are merged in LDS by the same rule and the
 //     chunk's (o, lse) is written: as the output when the sequence has one
 //     chunk, else as a partial for the merge kernel.
+// Two score variants named in section "Paged and ragged layouts: FlashInfer"
+// are runtime switches: a sliding window (only the newest `window` keys are
+// visible; the chunks cover just those pages) and logit soft-capping (each
+// scaled score x becomes cap * tanh(x / cap) before the softmax).
 // Merge kernel, one wave per (sequence, head): M = max lse, weights e^(lse-M),
 // fixed summation order, no atomics.
 #include "fa_device.hpp"
@@ -54,7 +58,17 @@ struct DecParams {
   float* part_lse;
   int B, H, Hkv, max_pages, num_pages, num_splits, max_splits;
   float c;   // scale * log2(e)
+  int window;            // > 0: only the newest `window` keys are visible
+  int softcap_on;        // 1: scores are soft-capped
+  float cap_over_scale;  // softcap / scale
+  float scale_over_cap;  // scale / softcap
 };
+
+// Keys visible to the query of a sequence of `len` cached tokens: positions
+// [first_visible(len, window), len).
+__device__ __forceinline__ int first_visible(int len, int window) {
+  return (window > 0 && len > window) ? len - window : 0;
+}
 
 __device__ __forceinline__ float nanf_() { return __builtin_nanf(""); }
 
@@ -128,11 +142,15 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecParams a) 
   const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
   const int len = a.seq_lens[b];
   const bool bad_len = len < 0 || len > a.max_pages * kPage;
-  const int nsplit = decode_splits(bad_len ? 0 : len, a.num_splits);
+  const int kv_start = bad_len ? 0 : first_visible(len, a.window);
+  const int nsplit = decode_splits(bad_len ? 0 : len - kv_start, a.num_splits);
   if (split >= nsplit) return;                 // whole workgroup: uniform
   const int npages = bad_len ? 0 : (len + kPage - 1) / kPage;
+  const int p0 = kv_start / kPage;             // first page holding a visible key
   int pb, pe;
-  split_pages(npages, nsplit, split, &pb, &pe);
+  split_pages(npages - p0, nsplit, split, &pb, &pe);
+  pb += p0;
+  pe += p0;
 
   const int64_t row_stride = static_cast<int64_t>(a.Hkv) * D;   // between token slots
   const int64_t page_stride = row_stride * kPage;
@@ -216,11 +234,18 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecParams a) 
             kl + hs * D + (((4 * c + grp) ^ kswz<D>(hs)) * 8));
         s = E::mma16(op, qop[c], s);
       }
+      if (a.softcap_on) {
+        // Soft-capped logit cap * tanh(scale * s / cap), kept in raw-score
+        // units so that the base-2 step below stays one FMA.
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[i] = a.cap_over_scale * tanhf(s[i] * a.scale_over_cap);
+      }
       const int valid = min(kPage, len - p * kPage);   // tokens of this page that exist
-      if (valid < kPage) {
+      const int lo = kv_start - p * kPage;             // tokens before this are outside the window
+      if (valid < kPage || lo > 0) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (4 * grp + i >= valid) s[i] = kNegInf;
+          if (4 * grp + i >= valid || 4 * grp + i < lo) s[i] = kNegInf;
       }
       float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
       mx = max_xor16(mx);
@@ -256,7 +281,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecParams a) 
         const uint4 raw = *reinterpret_cast<const uint4*>(vl + t * D + 8 * e);
         const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
         float vv[8];
-        const bool ok = t < valid;   // slots past the end may hold anything
+        const bool ok = t < valid && t >= lo;   // slots outside the visible range may hold anything
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           vv[2 * j] = ok ? E::to_f32(static_cast<uint16_t>(w[j] & 0xffffu)) : 0.f;
@@ -349,6 +374,7 @@ struct MergeParams {
   int heads;                  // decode mode: rows per sequence
   int fixed_splits;           // decode mode: num_splits argument
   int max_len;                // decode mode: max_pages * page_size
+  int window;                 // decode mode: visible-key window (0 = all)
 };
 
 constexpr int kMergeMaxS = 1024;
@@ -363,7 +389,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams a) {
   if (DECODE) {
     const int len = a.seq_lens[r / a.heads];
     const bool bad = len < 0 || len > a.max_len;
-    n = decode_splits(bad ? 0 : len, a.fixed_splits);
+    n = decode_splits(bad ? 0 : len - first_visible(len, a.window), a.fixed_splits);
     if (n <= 1) return;   // written directly by the decode kernel
   } else {
     n = a.num_parts ? a.num_parts[r] : a.S;
@@ -471,6 +497,10 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   p.max_pages = a.max_pages; p.num_pages = a.num_pages;
   p.num_splits = a.num_splits; p.max_splits = a.max_splits;
   p.c = a.scale * kLog2e;
+  p.window = a.window;
+  p.softcap_on = a.softcap > 0.f ? 1 : 0;
+  p.cap_over_scale = a.softcap > 0.f ? a.softcap / a.scale : 0.f;
+  p.scale_over_cap = a.softcap > 0.f ? a.scale / a.softcap : 0.f;
   const int G = a.H / a.Hkv;
   const dim3 grid(a.max_splits, a.Hkv, a.B);
   hipError_t e;
@@ -495,6 +525,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   m.heads = a.H;
   m.fixed_splits = a.num_splits;
   m.max_len = a.max_pages * kPage;
+  m.window = a.window;
   return merge_dispatch<true>(m, a.out_dtype, s);
 }
 
@@ -512,6 +543,7 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
   m.heads = 1;
   m.fixed_splits = 0;
   m.max_len = 0;
+  m.window = 0;
   return merge_dispatch<false>(m, a.out_dtype, s);
 }
 

@@ -34,6 +34,8 @@ struct DecodeArgs {
   int B, H, Hkv, d, page_size, max_pages, num_pages;
   float scale;
   int num_splits;  // 0 = per-sequence rule, else fixed
+  int window;      // > 0: only the newest `window` keys are visible
+  float softcap;   // > 0: scores x become softcap * tanh(x / softcap)
   fa_dtype dtype, out_dtype;
   float* part_o;    // [B, H, S, d] fp32
   float* part_lse;  // [B, H, S]    fp32

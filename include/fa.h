@@ -12,6 +12,11 @@
  *                      results are merged ("3.4 Attention Kernels", sections
  *                      "Decode attention and Flash-Decoding" and "Paged and
  *                      ragged layouts: FlashInfer").
+ *   fa_decode_paged_ex the same with a sliding window and logit soft-capping
+ *                      (section "Paged and ragged layouts: FlashInfer").
+ *   fa_decode_graph_*  a decode step recorded once as a HIP graph and replayed
+ *                      with one launch ("3.4 Attention Kernels", section
+ *                      "Kernel launch overhead and CUDA graphs").
  *   fa_merge_partials  the merge of partial results computed on disjoint key
  *                      sets ("3.4 Attention Kernels", section "Online softmax",
  *                      last paragraph).
@@ -75,8 +80,8 @@ typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
  * j is visible to query i iff j <= i + (Nk - Nq): the causal diagonal is
  * aligned to the bottom-right corner, as in the page's naive_attention code,
  * which equals the usual alignment when Nq == Nk. Key tiles that lie wholly
- * above the diagonal are never read ("tiles entirely above the diagonal are
- * skipped").
+ * above the diagonal are never read (the causal tile skipping of section
+ * "FlashAttention: tiling").
  *
  * Layouts (row-major, contiguous):
  *   Q   [B, Nq, H,   d]  in_dtype
@@ -163,6 +168,83 @@ fa_status fa_decode_paged(const void* q, const void* K_pool,
                           int num_splits, fa_dtype dtype, fa_dtype out_dtype,
                           void* workspace, size_t workspace_bytes,
                           void* stream);
+
+/*
+ * fa_decode_paged_ex - fa_decode_paged with two score variants, the sliding
+ * window and logit soft-capping that section "Paged and ragged layouts:
+ * FlashInfer" of "3.4 Attention Kernels" lists among the attention variants.
+ * The page does not define them; this library's readings are:
+ *   window > 0   only the newest `window` cached tokens of each sequence are
+ *                visible, i.e. tokens t with seq_lens[b] - window <= t <
+ *                seq_lens[b] (the query's own token counts as one of them);
+ *                window == 0 means all tokens. Pages before the window are
+ *                neither split over nor read, and their block-table entries
+ *                are ignored.
+ *   softcap > 0  each scaled score x = scale * q.k is replaced by
+ *                softcap * tanh(x / softcap) before the softmax; LSE is the
+ *                log-sum-exp of the capped scores. softcap == 0 disables it.
+ * The chunk count of a sequence is fa_decode_num_splits(v, num_splits) with
+ * v = the number of visible tokens (min(seq_lens[b], window) for window > 0).
+ * Everything else (layouts, workspace, support, contract, NaN on contract
+ * violation) is as for fa_decode_paged; window < 0 or a negative or
+ * non-finite softcap returns FA_ERR_BAD_ARG. With window == 0 and
+ * softcap == 0 the results equal fa_decode_paged's bit for bit.
+ */
+fa_status fa_decode_paged_ex(const void* q, const void* K_pool,
+                             const void* V_pool, const int32_t* block_table,
+                             const int32_t* seq_lens, void* O, float* LSE,
+                             int B, int H, int Hkv, int d, int page_size,
+                             int max_pages_per_seq, int num_pages, float scale,
+                             int num_splits, int window, float softcap,
+                             fa_dtype dtype, fa_dtype out_dtype,
+                             void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/*
+ * A decode step recorded once and replayed with one launch.
+ *
+ * "3.4 Attention Kernels", section "Kernel launch overhead and CUDA graphs":
+ * a step made of short kernels is bound by the host's launch rate; recording
+ * the launches once and replaying them as a graph removes that cost, provided
+ * shapes and buffer addresses stay fixed, and callers copy each step's inputs
+ * into the same buffers.
+ *
+ * fa_decode_graph_create validates exactly what fa_decode_paged_ex validates
+ * (same arguments, same status codes, nothing recorded on error), then records
+ * the decode kernel and, when chunks are merged, the merge kernel on a private
+ * stream into an instantiated HIP graph, stored in *out. The graph binds the
+ * pointers and sizes given here: every buffer must stay allocated, unmoved and
+ * sized as given until fa_decode_graph_destroy. Contents may change between
+ * launches (new q, new cache tokens, new seq_lens and block_table entries
+ * within the recorded max_pages_per_seq and num_pages); each launch reads the
+ * buffers as they are when it runs. Creating allocates host and driver
+ * objects (graph, executable graph, a temporary stream); launching allocates
+ * nothing. Failures of the HIP graph API return FA_ERR_HIP and leave *out
+ * NULL.
+ *
+ * fa_decode_graph_launch enqueues one replay on `stream` (hipStream_t as
+ * void*, NULL = default stream); results equal those of the eager call on
+ * the same buffer contents, bit for bit. Replays of one graph must not
+ * overlap in time on different streams (they share O, LSE and workspace).
+ * A NULL graph returns FA_ERR_NULL_PTR.
+ *
+ * fa_decode_graph_destroy frees the graph; NULL is a no-op. The caller must
+ * make sure no enqueued replay is still running.
+ */
+typedef struct fa_decode_graph fa_decode_graph;
+
+fa_status fa_decode_graph_create(fa_decode_graph** out, const void* q,
+                                 const void* K_pool, const void* V_pool,
+                                 const int32_t* block_table,
+                                 const int32_t* seq_lens, void* O, float* LSE,
+                                 int B, int H, int Hkv, int d, int page_size,
+                                 int max_pages_per_seq, int num_pages,
+                                 float scale, int num_splits, int window,
+                                 float softcap, fa_dtype dtype,
+                                 fa_dtype out_dtype, void* workspace,
+                                 size_t workspace_bytes);
+fa_status fa_decode_graph_launch(const fa_decode_graph* graph, void* stream);
+void fa_decode_graph_destroy(fa_decode_graph* graph);
 
 /*
  * fa_merge_partials - merge partial results over disjoint key sets.

@@ -9,6 +9,7 @@ from .attention_ref import (  # noqa: F401
     attention,
     causal_visible,
     decode_paged,
+    decode_paged_variant,
     default_threads,
     gather_paged_kv,
     log_sum_exp,

@@ -22,7 +22,7 @@ its NumPy `naive_attention` under "Code"):
 Everything is evaluated in float64 on the (already dtype-rounded) inputs the
 GPU receives; bf16/fp16/fp32 values are exact in float64.
 
-Readings taken where the pages leave a point open (each is listed in the design doc):
+Readings taken where the pages leave a point open:
   * Layout [batch, seq, heads, d] for Q/K/V/O ("3.4 Attention Kernels",
     "Paged and ragged layouts"), LSE as [batch, heads, seq].
   * Causal alignment is bottom-right: key j is visible to query i iff
@@ -57,6 +57,7 @@ __all__ = [
     "attention",
     "log_sum_exp",
     "decode_paged",
+    "decode_paged_variant",
     "gather_paged_kv",
     "merge_partials",
     "online_softmax_row",
@@ -286,6 +287,58 @@ def decode_paged(q, k_pool, v_pool, block_table, seq_lens, scale: float):
                                scale, False, np.zeros(1, np.int64), 1)
             out[b, h] = o[0]
             lse[b, h] = l[0]
+    return out, lse
+
+
+def _window_start(seq_len: int, window: int) -> int:
+    """First visible token of a sequence of seq_len tokens under a sliding
+    window of the newest `window` tokens (0 = no window)."""
+    return seq_len - window if (window > 0 and seq_len > window) else 0
+
+
+def _soft_cap(x: np.ndarray, cap: float) -> np.ndarray:
+    """Logit soft-capping of scaled scores: cap * tanh(x / cap)."""
+    return cap * np.tanh(x / cap)
+
+
+def decode_paged_variant(q, k_pool, v_pool, block_table, seq_lens, scale: float,
+                         window: int = 0, softcap: float = 0.0):
+    """Decode attention with a sliding window and/or logit soft-capping.
+
+    "3.4 Attention Kernels", section "Paged and ragged layouts: FlashInfer",
+    names both as attention variants without defining them; the readings here
+    are:
+      window > 0: only the newest `window` tokens t of sequence b are visible,
+        seq_lens[b] - window <= t < seq_lens[b] (the query's own position is
+        the newest token); window == 0: all tokens.
+      softcap > 0: the scaled score x = scale * q.k becomes
+        softcap * tanh(x / softcap) before the softmax; softcap == 0: unchanged.
+    Then P = exp(x - max x), O = P V / sum P, LSE = max x + ln sum P over the
+    visible tokens, as in `decode_paged`. Returns O [B, H, d], LSE [B, H].
+    """
+    q = _f64(q)
+    B, H, d = q.shape
+    hkv = k_pool.shape[2]
+    if H % hkv:
+        raise ValueError("query heads must be a multiple of KV heads")
+    group = H // hkv
+    out = np.zeros((B, H, d))
+    lse = np.full((B, H), -np.inf)
+    for b in range(B):
+        L = int(seq_lens[b])
+        first = _window_start(L, window)
+        if L - first <= 0:
+            continue
+        kb = gather_paged_kv(k_pool, block_table, L, b)[first:]
+        vb = gather_paged_kv(v_pool, block_table, L, b)[first:]
+        for h in range(H):
+            hk = h // group
+            x = _scores(q[b, h][None, :], kb[:, hk, :], scale)   # [1, visible]
+            if softcap > 0:
+                x = _soft_cap(x, softcap)
+            m, p, l = _softmax_stats(x)
+            out[b, h] = (p @ vb[:, hk, :])[0] / l[0]
+            lse[b, h] = _lse_from_stats(m, l)[0]
     return out, lse
 
 

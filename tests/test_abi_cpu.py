@@ -103,6 +103,48 @@ def test_decode_validation(kw, status):
     assert dec(**kw) == status
 
 
+def dec_ex(window=0, softcap=0.0, B=2, H=8, Hkv=2, d=128, page=16, max_pages=4, num_pages=8,
+           scale=0.1, splits=0, dt=BF16, outd=BF16, ptrs=(None,) * 7, ws=None, ws_bytes=0):
+    return fa.lib().fa_decode_paged_ex(*ptrs, B, H, Hkv, d, page, max_pages, num_pages, scale,
+                                       splits, window, softcap, dt, outd, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(window=-1), ARG), (dict(softcap=-1.0), ARG), (dict(softcap=float("nan")), ARG),
+    (dict(softcap=float("inf")), ARG), (dict(window=5, B=0), OK), (dict(softcap=30.0), NULL),
+    (dict(window=4096, softcap=50.0, d=96), UNSUP), (dict(window=3, splits=17), ARG),
+    (dict(B=-1, window=1), SHAPE), (dict(window=1, B=0), OK),
+])
+def test_decode_ex_validation(kw, status):
+    assert dec_ex(**kw) == status
+
+
+def test_decode_ex_workspace_checks():
+    p = [FAKE] * 7
+    need = fa.decode_workspace_size(2, 8, 128, 16)
+    assert dec_ex(window=100, ptrs=p, ws=None, ws_bytes=need) == WS
+    assert dec_ex(window=100, ptrs=p, ws=FAKE, ws_bytes=need - 1) == WS
+
+
+def test_decode_graph_validation_before_any_hip_call():
+    lib = fa.lib()
+    p = [FAKE] * 7
+    h = ctypes.c_void_p()
+
+    def create(out, window=0, softcap=0.0, splits=0, ptrs=p, B=2, ws=None, ws_bytes=0):
+        return lib.fa_decode_graph_create(out, *ptrs, B, 8, 2, 128, 16, 4, 8, 0.1, splits,
+                                          window, softcap, BF16, BF16, ws, ws_bytes)
+    assert create(None) == NULL
+    assert create(ctypes.byref(h), window=-1) == ARG
+    assert h.value is None
+    assert create(ctypes.byref(h), softcap=float("nan")) == ARG
+    assert create(ctypes.byref(h), splits=17) == ARG
+    assert create(ctypes.byref(h), ptrs=[None] * 7) == NULL
+    assert create(ctypes.byref(h), ws=None, ws_bytes=0) == WS
+    assert lib.fa_decode_graph_launch(None, None) == NULL
+    lib.fa_decode_graph_destroy(None)
+
+
 def test_decode_workspace_checks():
     p = [FAKE] * 7
     need = fa.decode_workspace_size(2, 8, 128, 16)

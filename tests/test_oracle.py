@@ -324,6 +324,90 @@ def pin_paged_decode(ref):
     np.testing.assert_array_equal(lse, l2)
 
 
+def _paged_case(rng, lens, B=3, H=4, hkv=2, d=8, page=16, extra_pages=3):
+    max_pages = int(max(1, -(-max(lens) // page)))
+    n_pages = B * max_pages + extra_pages
+    kp, vp = _rand(rng, n_pages, page, hkv, d), _rand(rng, n_pages, page, hkv, d)
+    q = _rand(rng, B, H, d)
+    table = rng.permutation(n_pages)[:B * max_pages].reshape(B, max_pages).copy()
+    return q, kp, vp, table, np.asarray(lens)
+
+
+def _tokens(pool, table, b, t, page=16):
+    return pool[table[b, t // page], t % page]
+
+
+def pin_decode_window(ref):
+    """Sliding window: the newest `window` tokens only. window >= len is the
+    plain decode; window == 1 returns the newest token's value row with
+    LSE = its scaled score; 1 < window < len equals dense attention over the
+    explicitly sliced last `window` tokens; len 0 gives O = 0, LSE = -inf."""
+    rng = np.random.default_rng(31)
+    lens = [45, 16, 0]
+    q, kp, vp, table, lens = _paged_case(rng, lens)
+    scale = 0.4
+    plain = ref.decode_paged(q, kp, vp, table, lens, scale)
+    for w in (45, 46, 1000):
+        o, l = ref.decode_paged_variant(q, kp, vp, table, lens, scale, window=w)
+        np.testing.assert_allclose(o, plain[0], rtol=0, atol=1e-14)
+        np.testing.assert_allclose(l, plain[1], rtol=0, atol=1e-14)
+    o, l = ref.decode_paged_variant(q, kp, vp, table, lens, scale, window=1)
+    for b in range(2):
+        t = lens[b] - 1
+        kl, vl = _tokens(kp, table, b, t), _tokens(vp, table, b, t)
+        for h in range(4):
+            np.testing.assert_array_equal(o[b, h], vl[h // 2])
+            assert abs(l[b, h] - scale * float(q[b, h] @ kl[h // 2])) < 1e-13
+    assert np.all(o[2] == 0) and np.all(l[2] == -np.inf)
+    for w in (2, 7, 17, 30):
+        o, l = ref.decode_paged_variant(q, kp, vp, table, lens, scale, window=w)
+        for b in range(2):
+            t = np.arange(max(0, lens[b] - w), lens[b])
+            kb, vb = _tokens(kp, table, b, t), _tokens(vp, table, b, t)
+            od, ld = ref.attention(q[b][None, None], kb[None], vb[None], scale, False)
+            np.testing.assert_allclose(o[b], od[0, 0], rtol=0, atol=1e-13)
+            np.testing.assert_allclose(l[b], ld[0, :, 0], rtol=0, atol=1e-13)
+
+
+def pin_decode_softcap(ref):
+    """Logit soft-capping cap*tanh(x/cap) of the scaled scores: a two-key
+    closed form worked by hand; an enormous cap is the plain decode; with
+    every score huge and positive all capped scores equal cap, so the weights
+    are uniform, O is the mean value row and LSE = cap + ln(len)."""
+    # two keys, d = 2, one head: raw dots 3 and -1, scale 0.5, cap 2
+    q = np.array([[[1.0, 0.0]]])
+    kp = np.zeros((1, 16, 1, 2))
+    vp = np.zeros((1, 16, 1, 2))
+    kp[0, 0, 0] = [3.0, 5.0]
+    kp[0, 1, 0] = [-1.0, 2.0]
+    vp[0, 0, 0] = [1.0, -2.0]
+    vp[0, 1, 0] = [4.0, 0.5]
+    c1, c2 = 2.0 * math.tanh(0.75), 2.0 * math.tanh(-0.25)
+    w1, w2 = math.exp(c1), math.exp(c2)
+    o, l = ref.decode_paged_variant(q, kp, vp, np.array([[0]]), np.array([2]), 0.5,
+                                    softcap=2.0)
+    np.testing.assert_allclose(o[0, 0], [(w1 * 1 + w2 * 4) / (w1 + w2),
+                                         (w1 * -2 + w2 * 0.5) / (w1 + w2)], rtol=1e-14)
+    assert abs(l[0, 0] - math.log(w1 + w2)) < 1e-14
+    rng = np.random.default_rng(32)
+    lens = [45, 16, 0]
+    qq, kk, vv, table, lens = _paged_case(rng, lens)
+    plain = ref.decode_paged(qq, kk, vv, table, lens, 0.3)
+    o, l = ref.decode_paged_variant(qq, kk, vv, table, lens, 0.3, softcap=1e9)
+    np.testing.assert_allclose(o, plain[0], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l, plain[1], rtol=0, atol=1e-12)
+    # all keys aligned with the query and huge: every capped score is 5
+    kk2 = np.abs(kk) + 1.0
+    qh = np.full_like(qq, 1e6)
+    o, l = ref.decode_paged_variant(qh, kk2, vv, table, lens, 1.0, softcap=5.0)
+    for b in range(2):
+        t = np.arange(lens[b])
+        vb = _tokens(vv, table, b, t)
+        for h in range(4):
+            np.testing.assert_allclose(o[b, h], vb[:, h // 2].mean(axis=0), rtol=0, atol=1e-12)
+            assert abs(l[b, h] - (5.0 + math.log(lens[b]))) < 1e-12
+
+
 def pin_merge(ref):
     """The merge rule: split partials merged == unsplit, for 1..96 splits
     (more splits than keys gives empty parts); associative; order-free;
@@ -396,7 +480,7 @@ PINS = [pin_lab_example, pin_trace_example, pin_rescale_factor, pin_single_key,
         pin_causal_row0, pin_constant_v, pin_zero_query, pin_rows_sum_to_one,
         pin_brute_force, pin_torch_sdpa, pin_key_permutation,
         pin_gqa_equals_repeated_mha, pin_rows_subset, pin_paged_decode,
-        pin_merge, pin_large_scores]
+        pin_decode_window, pin_decode_softcap, pin_merge, pin_large_scores]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -523,7 +607,25 @@ def _mut_page_slot(m):
     m.setattr(ref_mod, "gather_paged_kv", f)
 
 
-MUTANTS = [_mut_causal_flipped, _mut_causal_off_by_one, _mut_causal_top_left,
+def _mut_window_off_by_one(m):
+    m.setattr(ref_mod, "_window_start",
+              lambda L, w: L - w + 1 if (w > 0 and L > w) else 0)
+
+
+def _mut_window_oldest(m):
+    m.setattr(ref_mod, "_window_start", lambda L, w: 0)
+
+
+def _mut_softcap_unscaled(m):
+    m.setattr(ref_mod, "_soft_cap", lambda x, cap: np.tanh(x / cap))
+
+
+def _mut_softcap_no_tanh(m):
+    m.setattr(ref_mod, "_soft_cap", lambda x, cap: np.clip(x, -cap, cap))
+
+
+MUTANTS = [_mut_window_off_by_one, _mut_window_oldest, _mut_softcap_unscaled,
+           _mut_softcap_no_tanh, _mut_causal_flipped, _mut_causal_off_by_one, _mut_causal_top_left,
            _mut_no_scale, _mut_transposed_scores, _mut_no_max_subtraction,
            _mut_lse_base2, _mut_lse_without_max, _mut_dropped_sum_term, _mut_gqa_modulo,
            _mut_merge_sign, _mut_merge_no_weights,

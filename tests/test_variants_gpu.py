@@ -1,0 +1,190 @@
+"""Parity of the decode variants (sliding window, logit soft-capping) with the
+float64 oracle, through the C ABI.
+
+Every case prints what it runs before touching the GPU. Tokens outside the
+window hold NaN and their block-table entries point outside the pool: the
+kernels must never use them.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import exact_tiled_attention_11_amd as fa
+from exact_tiled_attention_11_amd import inputs
+import oracle
+from parity_utils import assert_lowp_acc, assert_lowp_out, assert_lse, assert_rounded_from, np64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TD = inputs.TORCH_DTYPES
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def hide_outside_window(pi, lens, window):
+    """NaN in every token slot before each sequence's window; table entries of
+    pages wholly before the window point outside the pool."""
+    n_pages = pi.k_pool.shape[0]
+    for b, L in enumerate(lens):
+        first = L - window if (window > 0 and L > window) else 0
+        for t0 in range(0, first, 16):
+            pg = int(pi.block_table[b, t0 // 16])
+            hi = min(16, first - t0)
+            pi.k_pool[pg, :hi] = float("nan")
+            pi.v_pool[pg, :hi] = float("nan")
+        for p in range(first // 16):
+            pi.block_table[b, p] = n_pages + 7
+
+
+def to_dev(pi):
+    return dict(q=pi.q.to(DEV), k=pi.k_pool.to(DEV), v=pi.v_pool.to(DEV),
+                t=pi.block_table.to(DEV), s=pi.seq_lens.to(DEV))
+
+
+def gpu_decode_ex(d, window, softcap, splits, out_dtype=None):
+    say(f"  fa_decode_paged_ex B={d['q'].shape[0]} window={window} softcap={softcap} "
+        f"splits={splits} out={out_dtype}")
+    o, l = fa.decode_paged_ex(d["q"], d["k"], d["v"], d["t"], d["s"], window=window,
+                              softcap=softcap, num_splits=splits, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return o, l
+
+
+VAR = [
+    # (H, Hkv, d, dtype, lens)
+    (8, 8, 128, "bf16", [1, 15, 16, 17, 31, 33, 0, 300]),
+    (8, 4, 64, "f16", [0, 1, 100, 2048, 2049, 5000]),
+    (32, 8, 128, "bf16", [1, 2047, 4097, 9000, 16, 300]),
+]
+WINDOWS = [1, 16, 17, 100, 4096]
+
+
+@pytest.mark.parametrize("case", VAR, ids=[f"h{c[0]}/{c[1]}-d{c[2]}-{c[3]}" for c in VAR])
+@pytest.mark.parametrize("window", WINDOWS)
+@pytest.mark.parametrize("splits", [0, 1, 3, 16])
+def test_decode_window(case, window, splits):
+    H, Hkv, d, dt, lens = case
+    pi = inputs.paged_decode_inputs(len(lens), H, Hkv, d, lens, seed=41, dtype=TD[dt])
+    ro, rl = oracle.decode_paged_variant(pi.q, pi.k_pool, pi.v_pool, pi.block_table,
+                                         pi.seq_lens, 1 / math.sqrt(d), window=window)
+    hide_outside_window(pi, lens, window)
+    say(f"decode window {case} window={window} splits={splits}")
+    dev = to_dev(pi)
+    o32, l32 = gpu_decode_ex(dev, window, 0.0, splits, torch.float32)
+    o16, l16 = gpu_decode_ex(dev, window, 0.0, splits)
+    assert_lowp_acc(f"win {case} {window}", np64(o32), ro)
+    assert_lse(f"win {case} {window}", np64(l32), rl)
+    assert_rounded_from(f"win {case} {window}", o16, o32)
+    assert torch.equal(l16, l32)
+
+
+SOFTCAP = [(5.0, 0, 1.0), (30.0, 0, 30.0), (30.0, 100, 30.0), (50.0, 4096, 8.0)]
+
+
+@pytest.mark.parametrize("case", VAR, ids=[f"h{c[0]}/{c[1]}-d{c[2]}-{c[3]}" for c in VAR])
+@pytest.mark.parametrize("cap,window,qs", SOFTCAP, ids=[f"cap{c}-w{w}-q{q}" for c, w, q in SOFTCAP])
+@pytest.mark.parametrize("splits", [0, 3])
+def test_decode_softcap(case, cap, window, qs, splits):
+    H, Hkv, d, dt, lens = case
+    pi = inputs.paged_decode_inputs(len(lens), H, Hkv, d, lens, seed=42, dtype=TD[dt])
+    pi.q = (pi.q.float() * qs).to(pi.q.dtype)   # sharper scores so the cap matters
+    ro, rl = oracle.decode_paged_variant(pi.q, pi.k_pool, pi.v_pool, pi.block_table,
+                                         pi.seq_lens, 1 / math.sqrt(d), window=window,
+                                         softcap=cap)
+    hide_outside_window(pi, lens, window)
+    say(f"decode softcap {case} cap={cap} window={window} qscale={qs} splits={splits}")
+    dev = to_dev(pi)
+    o32, l32 = gpu_decode_ex(dev, window, cap, splits, torch.float32)
+    o16, _ = gpu_decode_ex(dev, window, cap, splits)
+    assert_lowp_acc(f"cap {case} {cap}", np64(o32), ro)
+    assert_lse(f"cap {case} {cap}", np64(l32), rl)
+    assert_rounded_from(f"cap {case} {cap}", o16, o32)
+
+
+def test_decode_ex_defaults_equal_plain_decode():
+    lens = [3000, 17, 4096, 1, 0, 777]
+    pi = inputs.paged_decode_inputs(len(lens), 32, 8, 128, lens, seed=43)
+    dev = to_dev(pi)
+    say("decode_ex defaults vs decode")
+    for splits in (0, 1, 5):
+        a = fa.decode_paged(dev["q"], dev["k"], dev["v"], dev["t"], dev["s"], num_splits=splits)
+        b = fa.decode_paged_ex(dev["q"], dev["k"], dev["v"], dev["t"], dev["s"],
+                               num_splits=splits)
+        torch.cuda.synchronize()
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_decode_window_softcap_b64_h32_kv8():
+    """The paged-decode workload with a 4096-token window and cap 50."""
+    p = inputs.WORKLOADS["paged_decode_bf16_b64_h32_kv8"].params
+    lens = inputs.uniform_lengths(p["B"], p["len_lo"], p["len_hi"], p["seed"])
+    pi = inputs.paged_decode_inputs(p["B"], p["H"], p["Hkv"], p["d"], lens, p["seed"],
+                                    pool_factor=p["pool_factor"], max_pages=p["len_hi"] // 16)
+    sel = np.arange(0, p["B"], 4)
+    say("c4 window 4096 cap 50: oracle on 16 sequences")
+    ro, rl = oracle.decode_paged_variant(pi.q[sel], pi.k_pool, pi.v_pool, pi.block_table[sel],
+                                         pi.seq_lens[sel], 1 / math.sqrt(128), window=4096,
+                                         softcap=50.0)
+    dev = to_dev(pi)
+    for splits in (0, 16):
+        o32, l32 = gpu_decode_ex(dev, 4096, 50.0, splits, torch.float32)
+        o16, _ = gpu_decode_ex(dev, 4096, 50.0, splits)
+        s = torch.as_tensor(sel)
+        assert_lowp_acc("c4 win/cap", np64(o32[s]), ro)
+        assert_lowp_out("c4 win/cap", o16[s], ro)
+        assert_lse("c4 win/cap", np64(l32[s]), rl)
+        assert_rounded_from("c4 win/cap", o16, o32)
+
+
+# ---------------------------------------------------------------------------
+# The decode step recorded as a HIP graph.
+# ---------------------------------------------------------------------------
+
+GRAPH = [
+    # (H, Hkv, d, dtype, lens, window, softcap, splits)
+    (32, 8, 128, "bf16", [1, 2047, 4097, 9000, 16, 300], 0, 0.0, 0),
+    (32, 8, 128, "bf16", [1, 2047, 4097, 9000, 16, 300], 0, 0.0, 1),
+    (8, 4, 64, "f16", [0, 1, 100, 2048, 2049, 5000], 1000, 30.0, 0),
+]
+
+
+@pytest.mark.parametrize("case", GRAPH, ids=[f"d{c[2]}-{c[3]}-w{c[5]}-cap{c[6]}-s{c[7]}"
+                                            for c in GRAPH])
+def test_decode_graph_replays_match_eager(case):
+    H, Hkv, d, dt, lens, window, cap, splits = case
+    B = len(lens)
+    pi = inputs.paged_decode_inputs(B, H, Hkv, d, lens, seed=44, dtype=TD[dt],
+                                    unreferenced="normal")
+    dev = to_dev(pi)
+    say(f"decode graph {case}: create")
+    g = fa.DecodeGraph(dev["q"], dev["k"], dev["v"], dev["t"], dev["s"], window=window,
+                       softcap=cap, num_splits=splits, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(45)
+    for it in range(4):
+        # a new step: new queries and shorter sequences, written into the bound buffers
+        qn = torch.from_numpy(rng.standard_normal(tuple(dev["q"].shape)).astype(np.float32))
+        dev["q"].copy_(qn.to(dev["q"].dtype))
+        new_lens = torch.as_tensor([max(0, L - 7 * it) for L in lens], dtype=torch.int32)
+        dev["s"].copy_(new_lens)
+        torch.cuda.synchronize()
+        say(f"  replay {it}: eager reference, then graph")
+        eo, el = fa.decode_paged_ex(dev["q"], dev["k"], dev["v"], dev["t"], dev["s"],
+                                    window=window, softcap=cap, num_splits=splits,
+                                    out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        go, gl = g.launch()
+        torch.cuda.synchronize()
+        assert torch.equal(go, eo) and torch.equal(gl, el), f"replay {it} differs from eager"
+        if it == 3:
+            ro, rl = oracle.decode_paged_variant(dev["q"].cpu(), pi.k_pool, pi.v_pool,
+                                                 pi.block_table, new_lens, 1 / math.sqrt(d),
+                                                 window=window, softcap=cap)
+            assert_lowp_acc("graph", np64(go), ro)
+            assert_lse("graph", np64(gl), rl)
+    g.close()
