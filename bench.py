@@ -194,6 +194,56 @@ def bench_decode_graph(torch, fa, inputs, dev, dp, n=200):
     return out
 
 
+def ragged_flops(q_lens, kv_lens, H, d, causal=True):
+    """4 d H x (visible query-key pairs); with causal, query i of a sequence sees
+    min(kv, max(0, i + kv - q + 1)) keys (bottom-right alignment)."""
+    pairs = 0.0
+    for ql, kl in zip(q_lens, kv_lens):
+        ql, kl = int(ql), int(kl)
+        off = kl - ql
+        if not causal:
+            pairs += ql * kl
+        elif off >= 0:
+            pairs += ql * (off + 1) + ql * (ql - 1) / 2.0
+        else:
+            pairs += sum(min(kl, max(0, i + off + 1)) for i in range(ql))
+    return 4.0 * d * H * pairs
+
+
+def bench_forward_paged(torch, fa, inputs, reps=10):
+    """Ragged queries over a paged cache: the causal-prefill shape with its K/V
+    scattered over pages, and a continuous-batching step mixing prefill chunks
+    with decode tokens."""
+    import numpy as np
+    out = {}
+    lens = inputs.uniform_lengths(60, 1024, 8192, 62)
+    cases = {
+        "causal_prefill_b4_h32_n8192_paged": ([8192] * 4, [8192] * 4, 32, 32),
+        "mixed_4x2048_prefill_60_decode_h32_kv8": ([2048] * 4 + [1] * 60,
+                                                   [8192] * 4 + list(lens), 32, 8),
+    }
+    for name, (ql, kl, H, Hkv) in cases.items():
+        ri = inputs.ragged_paged_inputs(ql, kl, H, Hkv, 128, seed=61, pool_factor=1.0,
+                                        unreferenced="normal")
+        args = [t.cuda() for t in (ri.q, ri.qo_indptr, ri.k_pool, ri.v_pool, ri.block_table,
+                                   ri.kv_lens)]
+        o = torch.empty_like(args[0])
+        lse = torch.empty((args[0].shape[0], H), dtype=torch.float32, device="cuda")
+
+        def run():
+            fa.forward_paged(*args, ri.max_q_len, causal=True, out=o, lse=lse)
+        for _ in range(2):
+            run()
+        ms = time_steps(torch, run, reps)
+        fl = ragged_flops(ql, kl, H, 128)
+        out[name] = {"ms_mean": ms, "algorithmic_flop": fl, "value": fl / (ms * 1e-3) / 1e12,
+                     "unit": "TFLOP/s", "frac_mfma": fl / (ms * 1e-3) / 1e12 /
+                     MFMA_BF16_PEAK_TFLOPS, "q_rows": int(sum(ql)), "kv_tokens": int(sum(kl))}
+        del args, o, lse, ri
+        torch.cuda.empty_cache()
+    return out
+
+
 def copy_calibration(torch, nbytes=1 << 30, reps=5):
     """A plain device copy of known size, for scaling HBM byte counters."""
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
@@ -211,9 +261,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--parts", default="prefill,decode,variants,graph",
+    ap.add_argument("--parts", default="prefill,decode,variants,graph,paged",
                     help="comma list: prefill, decode (the timed step), variants (windowed "
-                         "and soft-capped decode), graph (graph-replayed decode step)")
+                         "and soft-capped decode), graph (graph-replayed decode step), paged "
+                         "(ragged queries over a paged cache)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of each oracle baseline sample (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -308,6 +359,10 @@ def main():
         if "graph" in parts:
             log("bench: graph-replayed decode step")
             next_rows["decode_graph"] = bench_decode_graph(torch, fa, inputs, ddev, dp)
+
+    if "paged" in parts:
+        log("bench: ragged queries over a paged cache")
+        next_rows["forward_paged"] = bench_forward_paged(torch, fa, inputs)
 
     pre_tflops = flops / (pre_ms.mean() * 1e-3) / 1e12 if "prefill" in parts else None
     dec_gbps = kv_bytes / (dec_ms.mean() * 1e-3) / 1e9 if "decode" in parts else None

@@ -33,6 +33,8 @@ _I = ctypes.c_int
 _F = ctypes.c_float
 _SIGNATURES = {
     "fa_forward": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
+    "fa_forward_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I,
+                              _I, _F, _I, _I, _I, _P]),
     "fa_decode_num_splits": (_I, [_I, _I]),
     "fa_decode_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "fa_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I,
@@ -129,6 +131,37 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, out_dtype
                           B, H, Hkv, Nq, Nk, d, scale, int(bool(causal)), _code(q.dtype),
                           _code(out_dtype), _stream(q.device))
     _check(st, "fa_forward")
+    return out, lse
+
+
+def forward_paged(q, qo_indptr, k_pool, v_pool, block_table, kv_lens, max_q_len: int,
+                  causal: bool = False, scale: float | None = None, out_dtype=None, out=None,
+                  lse=None):
+    """Ragged queries over a paged cache. q [total_q,H,d]; qo_indptr [B+1] int32; pools
+    [P,16,Hkv,d]; block_table [B,max_pages] int32; kv_lens [B] int32
+    -> (O [total_q,H,d], LSE [total_q,H])."""
+    if q.dim() != 3 or k_pool.dim() != 4 or v_pool.shape != k_pool.shape:
+        raise ValueError("expected q [total_q,H,d] and pools [P,page,Hkv,d]")
+    total_q, H, d = q.shape
+    num_pages, page, Hkv = k_pool.shape[0], k_pool.shape[1], k_pool.shape[2]
+    B = kv_lens.shape[0]
+    if tuple(qo_indptr.shape) != (B + 1,) or block_table.dim() != 2 or \
+            block_table.shape[0] != B:
+        raise ValueError("qo_indptr must be [B+1] and block_table [B, max_pages]")
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((total_q, H, d), dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((total_q, H), dtype=torch.float32, device=q.device)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = lib().fa_forward_paged(
+        _dev(q, "q"), _dev(qo_indptr, "qo_indptr", torch.int32), _dev(k_pool, "k_pool", q.dtype),
+        _dev(v_pool, "v_pool", q.dtype), _dev(block_table, "block_table", torch.int32),
+        _dev(kv_lens, "kv_lens", torch.int32), _dev(out, "out", out_dtype),
+        _dev(lse, "lse", torch.float32), B, H, Hkv, d, total_q, int(max_q_len), page,
+        block_table.shape[1], num_pages, scale, int(bool(causal)), _code(q.dtype),
+        _code(out_dtype), _stream(q.device))
+    _check(st, "fa_forward_paged")
     return out, lse
 
 

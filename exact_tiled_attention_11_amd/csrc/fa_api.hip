@@ -20,6 +20,15 @@ bool scale_ok(float s) { return std::isfinite(s) && s > 0.f; }
 
 fa_status from_hip(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
+// Workgroups of a 16-bit forward launch: (batch, KV head) groups padded to a
+// multiple of the 8 XCDs, times the work units per group (blocks of 256
+// packed (query, head) rows; causal pairs two blocks per unit).
+int64_t forward16_grid(int64_t B, int64_t Hkv, int64_t group, int64_t max_q, bool causal) {
+  const int64_t blocks = (max_q * group + 255) / 256;
+  const int64_t units = causal ? (blocks + 1) / 2 : blocks;
+  return (B * Hkv + 7) / 8 * 8 * units;
+}
+
 // The kernels move data in 16-byte vectors.
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -53,15 +62,46 @@ fa_status fa_forward(const void* Q, const void* K, const void* V, void* O, float
   if (out_dtype != in_dtype && out_dtype != FA_F32) return FA_ERR_UNSUPPORTED;
   const int64_t q_elems = int64_t{B} * Nq * H * d;
   const int64_t kv_elems = int64_t{B} * Nk * Hkv * d;
-  const int64_t n_qblocks = (int64_t{Nq} + 127) / 128;
-  if (q_elems > kMaxElems || kv_elems > kMaxElems || int64_t{B} * H * n_qblocks > kMaxElems)
-    return FA_ERR_BAD_SHAPE;
+  const int64_t grid = in_dtype == FA_F32 ? int64_t{B} * H * ((int64_t{Nq} + 127) / 128)
+                                          : forward16_grid(B, Hkv, H / Hkv, Nq, causal != 0);
+  if (q_elems > kMaxElems || kv_elems > kMaxElems || grid > kMaxElems) return FA_ERR_BAD_SHAPE;
   if (B == 0 || Nq == 0) return FA_OK;
   if (!Q || !O || !LSE || (Nk > 0 && (!K || !V))) return FA_ERR_NULL_PTR;
   if (!aligned16(Q) || !aligned16(O) || (Nk > 0 && (!aligned16(K) || !aligned16(V))))
     return FA_ERR_BAD_ARG;
   fa::ForwardArgs a{Q, K, V, O, LSE, B, H, Hkv, Nq, Nk, d, scale, causal, in_dtype, out_dtype};
   return from_hip(fa::launch_forward(a, static_cast<hipStream_t>(stream)));
+}
+
+fa_status fa_forward_paged(const void* Q, const int32_t* qo_indptr, const void* K_pool,
+                           const void* V_pool, const int32_t* block_table, const int32_t* kv_lens,
+                           void* O, float* LSE, int B, int H, int Hkv, int d, int total_q,
+                           int max_q_len, int page_size, int max_pages_per_seq, int num_pages,
+                           float scale, int causal, fa_dtype dtype, fa_dtype out_dtype,
+                           void* stream) {
+  if (B < 0 || H < 1 || Hkv < 1 || H % Hkv != 0 || total_q < 0 || max_q_len < 0 ||
+      max_pages_per_seq < 1 || num_pages < 1 || page_size < 1)
+    return FA_ERR_BAD_SHAPE;
+  if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return FA_ERR_BAD_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_BAD_ARG;
+  if (!scale_ok(scale)) return FA_ERR_BAD_ARG;
+  if (!head_dim_ok(d) || page_size != FA_PAGE_SIZE || dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  if (out_dtype != dtype && out_dtype != FA_F32) return FA_ERR_UNSUPPORTED;
+  if (int64_t{total_q} * H * d > kMaxElems ||
+      int64_t{num_pages} * page_size * Hkv * d > kMaxElems ||
+      int64_t{B} * max_pages_per_seq > kMaxElems ||
+      int64_t{max_pages_per_seq} * page_size > kMaxElems ||
+      forward16_grid(B, Hkv, H / Hkv, max_q_len, causal != 0) > kMaxElems)
+    return FA_ERR_BAD_SHAPE;
+  if (B == 0 || total_q == 0 || max_q_len == 0) return FA_OK;
+  if (!Q || !qo_indptr || !K_pool || !V_pool || !block_table || !kv_lens || !O || !LSE)
+    return FA_ERR_NULL_PTR;
+  if (!aligned16(Q) || !aligned16(O) || !aligned16(K_pool) || !aligned16(V_pool))
+    return FA_ERR_BAD_ARG;
+  fa::ForwardPagedArgs a{Q, qo_indptr, K_pool, V_pool, block_table, kv_lens, O, LSE,
+                         B, H, Hkv, d, total_q, max_q_len, max_pages_per_seq, num_pages,
+                         scale, causal, dtype, out_dtype};
+  return from_hip(fa::launch_forward_paged(a, static_cast<hipStream_t>(stream)));
 }
 
 int fa_decode_num_splits(int seq_len, int num_splits) {

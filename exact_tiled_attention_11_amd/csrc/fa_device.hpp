@@ -164,4 +164,20 @@ __device__ __forceinline__ int xcd_remap(int p, int total) {
   return base + k;
 }
 
+// Workgroup id -> (group, unit) for work made of `groups` independent groups
+// (e.g. (sequence, KV head) pairs) of `units` workgroups each. XCD x (which
+// the dispatcher feeds the physical ids x, x + kXcds, ...) takes the groups
+// x, x + kXcds, x + 2 kXcds, ... one after the other, all units of a group in
+// order: a group's units share that XCD's L2, and groups of very different
+// cost (long and short sequences of a ragged batch) spread over all XCDs.
+// The grid has kXcds * ceil(groups / kXcds) * units workgroups; ids past the
+// last group return group = -1.
+__device__ __forceinline__ void xcd_group_unit(int p, int groups, int units, int* group,
+                                               int* unit) {
+  const int x = p % kXcds, k = p / kXcds;
+  const int g = x + kXcds * (k / units);
+  *unit = k % units;
+  *group = g < groups ? g : -1;
+}
+
 }  // namespace fa

@@ -52,9 +52,14 @@ struct FwdParams {
   int group;       // H / Hkv
   int n_qblocks;   // query blocks per (batch, head)
   int units;       // workgroup work units per (batch, head)
-  int total;       // B * H * units
+  int total;       // workgroups in the grid
   float c;         // scale * log2(e)
   int off;         // Nk - Nq: key j is visible to query i iff j <= i + off
+  // Ragged queries over a paged cache (K/V point at the page pools):
+  const int32_t* qo_indptr;    // [B + 1]: rows of sequence b are qo_indptr[b] ..
+  const int32_t* kv_lens;      // [B]
+  const int32_t* block_table;  // [B, max_pages]
+  int max_pages, num_pages, total_q, max_q_len;
 };
 
 // ---------------------------------------------------------------------------
@@ -119,6 +124,59 @@ struct TileLoader {
   }
 };
 
+// The same share of a K/V tile when the keys live in 16-token pages: key
+// k0 + row is slot row % 16 of page ids[row / 16] (a 64-key tile spans four
+// pages). Every slab lies inside one page.
+constexpr int kPageTokens = FA_PAGE_SIZE;
+
+__device__ __forceinline__ int pick_id(int4 ids, int i) {
+  return i == 0 ? ids.x : i == 1 ? ids.y : i == 2 ? ids.z : ids.w;
+}
+
+template <int D, int NW>
+struct PagedTileLoader {
+  static constexpr int CPR = D / 8;
+  static constexpr int RPS = 64 / CPR;                 // key rows per slab
+  static constexpr int SPW = kBC * CPR / 64 / NW;
+  static_assert(kPageTokens % RPS == 0, "a slab must not straddle pages");
+  int64_t roff[SPW];   // slot-in-page row offset + swizzled chunk offset
+  int coff[SPW];       // swizzled chunk offset alone
+  int row[SPW];
+  int slab0;
+
+  __device__ __forceinline__ PagedTileLoader(int64_t rs, int wave, int lane) {
+    slab0 = wave * SPW;
+#pragma unroll
+    for (int r = 0; r < SPW; ++r) {
+      const int slot = (slab0 + r) * 64 + lane;
+      row[r] = slot / CPR;
+      coff[r] = ((slot % CPR) ^ swz<D>(row[r])) * 8;
+      roff[r] = (row[r] % kPageTokens) * rs + coff[r];
+    }
+  }
+
+  // Rows past the last key re-read the last key, as in TileLoader.
+  __device__ __forceinline__ void load(const uint16_t* kbase, const uint16_t* vbase, int64_t rs,
+                                       int k0, int nk, int4 ids, uint16_t* kl,
+                                       uint16_t* vl) const {
+    const int64_t pstride = rs * kPageTokens;
+#pragma unroll
+    for (int r = 0; r < SPW; ++r) {
+      int64_t o;
+      if (k0 + kBC <= nk) {
+        const int id = pick_id(ids, (slab0 + r) * RPS / kPageTokens);
+        o = static_cast<int64_t>(id) * pstride + roff[r];
+      } else {
+        const int key = min(k0 + row[r], nk - 1);
+        const int id = pick_id(ids, key / kPageTokens - k0 / kPageTokens);
+        o = static_cast<int64_t>(id) * pstride + (key % kPageTokens) * rs + coff[r];
+      }
+      load_lds16_async(kbase + o, kl + (slab0 + r) * 512);
+      load_lds16_async(vbase + o, vl + (slab0 + r) * 512);
+    }
+  }
+};
+
 // Work unit of the 16-bit kernel. Non-causal: one query block. Causal: the
 // query blocks u and n-1-u of one (batch, head), one after the other, the
 // short one with keys in ascending tile order and the long one in descending
@@ -131,7 +189,7 @@ __device__ __forceinline__ int tile_count(int last_key) { return last_key >= 0 ?
 
 constexpr int kFwdStages = 2;   // LDS slots: tiles are loaded one step ahead
 
-template <class E, typename OutT, int D, bool CAUSAL, int NW>
+template <class E, typename OutT, int D, bool CAUSAL, int NW, bool PAGED>
 __global__ __launch_bounds__(NW * 64, 8 / NW)
 void fwd16_kernel(const FwdParams a) {
   constexpr int TILE = kBC * D;                 // elements per K or V tile
@@ -142,17 +200,46 @@ void fwd16_kernel(const FwdParams a) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[ST][2][TILE];   // [slot][K, V]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int L = xcd_remap(static_cast<int>(blockIdx.x), a.total);
-  const int bh = L / a.units;
-  const int u = L - bh * a.units;
-  const int b = bh / a.H, h = bh - b * a.H, hk = h / a.group;
+  int bh, u;
+  xcd_group_unit(static_cast<int>(blockIdx.x), a.B * a.Hkv, a.units, &bh, &u);
+  if (bh < 0) return;   // padding of the grid: whole workgroup
+  const int b = bh / a.Hkv, hk = bh - b * a.Hkv;
+  const int G = a.group;   // query heads per KV head
+
+  // Sequence geometry: Nq query rows starting at row q_row0 of Q and O, Nk keys.
+  // The workgroup serves KV head hk; its rows are the packed pairs (query i,
+  // head hk*G + g), row r = i*G + g, so every K/V tile is loaded once for the
+  // whole head group and a short query (a decode token) fills G rows, not a
+  // block.
+  int Nq, Nk, nqb;
+  int64_t q_row0;
+  bool bad = false;   // device-side contract violation: this sequence's outputs are NaN
+  if constexpr (PAGED) {
+    const int qs = a.qo_indptr[b], qe = a.qo_indptr[b + 1];
+    if (qs < 0 || qe < qs || qe > a.total_q) return;   // rows unknown: nothing is written
+    Nq = qe - qs;
+    q_row0 = qs;
+    Nk = a.kv_lens[b];
+    if (Nk < 0 || Nk > a.max_pages * kPageTokens || Nq > a.max_q_len) {
+      bad = true;
+      Nk = 0;
+    }
+  } else {
+    Nq = a.Nq;
+    Nk = a.Nk;
+    q_row0 = static_cast<int64_t>(b) * a.Nq;
+  }
+  const int nrows = Nq * G;   // packed rows of this (sequence, KV head)
+  nqb = (nrows + BR - 1) / BR;
+  const int off = Nk - Nq;
+  if (u >= (CAUSAL ? (nqb + 1) / 2 : nqb)) return;   // whole workgroup: uniform
 
   const int qb_first = u;
-  const int qb_second = CAUSAL ? a.n_qblocks - 1 - u : u;
+  const int qb_second = CAUSAL ? nqb - 1 - u : u;
   const int nseg = (CAUSAL && qb_second > qb_first) ? 2 : 1;
   auto block_tiles = [&](int qb) {
-    int last = a.Nk - 1;
-    if (CAUSAL) last = min(last, qb * BR + BR - 1 + a.off);
+    int last = Nk - 1;
+    if (CAUSAL) last = min(last, min(qb * BR + BR, nrows) / G - 1 + off);
     return tile_count(last);
   };
   const int n0 = block_tiles(qb_first);
@@ -164,10 +251,38 @@ void fwd16_kernel(const FwdParams a) {
 
   const int64_t q_rs = static_cast<int64_t>(a.H) * D;
   const int64_t kv_rs = static_cast<int64_t>(a.Hkv) * D;
-  const uint16_t* kbase = static_cast<const uint16_t*>(a.k) +
-                          static_cast<int64_t>(b) * a.Nk * kv_rs + static_cast<int64_t>(hk) * D;
-  const uint16_t* vbase = static_cast<const uint16_t*>(a.v) +
-                          static_cast<int64_t>(b) * a.Nk * kv_rs + static_cast<int64_t>(hk) * D;
+  const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + static_cast<int64_t>(hk) * D;
+  const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + static_cast<int64_t>(hk) * D;
+  if constexpr (!PAGED) {
+    kbase += static_cast<int64_t>(b) * a.Nk * kv_rs;
+    vbase += static_cast<int64_t>(b) * a.Nk * kv_rs;
+  }
+  // Paged: the four page ids of a tile are fetched one step before its loads
+  // are issued and made wave-uniform only when used, after the step's barrier
+  // (so the wait for them never holds back K/V loads in flight). Ids past the
+  // sequence's last page are never used (rows past the last key re-read that
+  // key); an id outside the pool is replaced by page 0 and marks the sequence
+  // bad.
+  const int32_t* table = PAGED ? a.block_table + static_cast<int64_t>(b) * a.max_pages : nullptr;
+  const int last_page = Nk > 0 ? (Nk - 1) / kPageTokens : 0;
+  bool bad_page = false;
+  auto fetch_ids = [&](int t) {
+    return make_int4(table[min(t * 4, last_page)], table[min(t * 4 + 1, last_page)],
+                     table[min(t * 4 + 2, last_page)], table[min(t * 4 + 3, last_page)]);
+  };
+  auto use_ids = [&](int4 raw) {
+    int v[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int id = __builtin_amdgcn_readfirstlane(v[i]);
+      if (id < 0 || id >= a.num_pages) {
+        bad_page = true;
+        id = 0;
+      }
+      v[i] = id;
+    }
+    return make_int4(v[0], v[1], v[2], v[3]);
+  };
 
   // Per-lane LDS read geometry.
   const int kr = lane & 31;                 // K operand row within a 32-key block
@@ -180,11 +295,19 @@ void fwd16_kernel(const FwdParams a) {
   const int vin = (r16 & 1) * 4;                          // element within the chunk
 
   const TileLoader<D, NW> loader(kv_rs, wave, lane);
-#pragma unroll
-  for (int t = 0; t < ST - 1; ++t)
-    if (t < n_steps)
-      loader.template load<true>(kbase, vbase, kv_rs, tile_at(t) * kBC, a.Nk, &smem[t][0][0],
-                                 &smem[t][1][0]);
+  const PagedTileLoader<D, NW> ploader(kv_rs, wave, lane);
+  int4 ids_next = make_int4(0, 0, 0, 0);   // fetched page ids of the tile of step g + 1
+  static_assert(ST == 2, "the page-id prefetch assumes tiles load one step ahead");
+  if (n_steps > 0) {
+    if constexpr (PAGED) {
+      ploader.load(kbase, vbase, kv_rs, tile_at(0) * kBC, Nk, use_ids(fetch_ids(tile_at(0))),
+                   &smem[0][0][0], &smem[0][1][0]);
+      if (n_steps > 1) ids_next = fetch_ids(tile_at(1));
+    } else {
+      loader.template load<true>(kbase, vbase, kv_rs, tile_at(0) * kBC, Nk, &smem[0][0][0],
+                                 &smem[0][1][0]);
+    }
+  }
 
   int g = 0;                   // step counter over both blocks
   int buf = 0;                 // slot of the tile of step g
@@ -192,21 +315,25 @@ void fwd16_kernel(const FwdParams a) {
   for (int seg = 0; seg < nseg; ++seg) {
     const int qb = seg == 0 ? qb_first : qb_second;
     const int nt = seg == 0 ? n0 : n1;
-    const int q0 = qb * BR;
-    const int qw0 = q0 + wave * kQPW;
-    const int qrow = qw0 + (lane & 31);
-    const int wave_last = CAUSAL ? min(a.Nk - 1, qw0 + kQPW - 1 + a.off) : a.Nk - 1;
+    const int qw0 = qb * BR + wave * kQPW;   // first packed row of this wave
+    const int prow = qw0 + (lane & 31);      // this lane's packed row
+    const int qrow = prow / G;               // its query position ...
+    const int h = hk * G + (prow - qrow * G);   // ... and query head
+    // Last key any row of this wave sees; -1 for a wave without real rows.
+    const int wave_last = qw0 >= nrows ? -1
+                          : CAUSAL ? min(Nk - 1, (min(qw0 + kQPW, nrows) - 1) / G + off)
+                                   : Nk - 1;
 
     // Q^T operand: lane l holds Q[row][16c + 8(l/32) .. +8].
     typename E::vec8 qf[QF];
     {
       const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
-                           (static_cast<int64_t>(b) * a.Nq + qrow) * q_rs +
+                           (q_row0 + qrow) * q_rs +
                            static_cast<int64_t>(h) * D + 8 * (lane >> 5);
 #pragma unroll
       for (int c = 0; c < QF; ++c) {
         uint4 v4 = make_uint4(0, 0, 0, 0);
-        if (qrow < a.Nq) v4 = *reinterpret_cast<const uint4*>(qp + 16 * c);
+        if (qrow < Nq) v4 = *reinterpret_cast<const uint4*>(qp + 16 * c);
         qf[c] = __builtin_bit_cast(typename E::vec8, v4);
       }
     }
@@ -225,9 +352,16 @@ void fwd16_kernel(const FwdParams a) {
     for (int j = 0; j < nt; ++j, ++g) {
       const int k0 = (seg == 0 ? j : nt - 1 - j) * kBC;
       const bool more = g + ST - 1 < n_steps;
-      if (more)
-        loader.template load<true>(kbase, vbase, kv_rs, tile_at(g + ST - 1) * kBC, a.Nk,
-                                   &smem[nbuf][0][0], &smem[nbuf][1][0]);
+      if (more) {
+        if constexpr (PAGED) {
+          ploader.load(kbase, vbase, kv_rs, tile_at(g + 1) * kBC, Nk, use_ids(ids_next),
+                       &smem[nbuf][0][0], &smem[nbuf][1][0]);
+          if (g + 2 < n_steps) ids_next = fetch_ids(tile_at(g + 2));
+        } else {
+          loader.template load<true>(kbase, vbase, kv_rs, tile_at(g + ST - 1) * kBC, Nk,
+                                     &smem[nbuf][0][0], &smem[nbuf][1][0]);
+        }
+      }
       if (k0 <= wave_last) {
         const uint16_t* kl = &smem[buf][0][0];
         const uint16_t* vl = &smem[buf][1][0];
@@ -254,9 +388,9 @@ void fwd16_kernel(const FwdParams a) {
           }
         }
 
-        const bool need_mask = (k0 + kBC > a.Nk) || (CAUSAL && k0 + kBC - 1 > qw0 + a.off);
+        const bool need_mask = (k0 + kBC > Nk) || (CAUSAL && k0 + kBC - 1 > qw0 / G + off);
         if (need_mask) {
-          const int lim = CAUSAL ? min(a.Nk - 1, qrow + a.off) : a.Nk - 1;
+          const int lim = CAUSAL ? min(Nk - 1, qrow + off) : Nk - 1;
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -337,9 +471,14 @@ void fwd16_kernel(const FwdParams a) {
     }
 
     const float l_tot = sum_xor32(l_run);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    if (qrow < a.Nq) {
-      OutT* orow = static_cast<OutT*>(a.o) + (static_cast<int64_t>(b) * a.Nq + qrow) * q_rs +
+    float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    float lse_v = l_tot > 0.f ? (m2_run + log2f(l_tot)) * kLn2 : kNegInf;
+    if (PAGED && (bad || bad_page)) {
+      inv = __builtin_nanf("");
+      lse_v = __builtin_nanf("");
+    }
+    if (qrow < Nq) {
+      OutT* orow = static_cast<OutT*>(a.o) + (q_row0 + qrow) * q_rs +
                    static_cast<int64_t>(h) * D;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
@@ -347,9 +486,10 @@ void fwd16_kernel(const FwdParams a) {
         for (int gg = 0; gg < 4; ++gg)
           store4(orow + 32 * db + 8 * gg + 4 * khi, acc[db][4 * gg] * inv,
                  acc[db][4 * gg + 1] * inv, acc[db][4 * gg + 2] * inv, acc[db][4 * gg + 3] * inv);
-      if (lane < 32)
-        a.lse[(static_cast<int64_t>(b) * a.H + h) * a.Nq + qrow] =
-            l_tot > 0.f ? (m2_run + log2f(l_tot)) * kLn2 : kNegInf;
+      // LSE layout: [B, H, Nq] dense; [total_q, H] for ragged queries.
+      const int64_t li = PAGED ? (q_row0 + qrow) * a.H + h
+                               : (static_cast<int64_t>(b) * a.H + h) * Nq + qrow;
+      if (lane < 32) a.lse[li] = lse_v;
     }
   }
 }
@@ -576,14 +716,14 @@ hipError_t launch_t(const FwdParams& p, bool causal, hipStream_t s) {
 
 constexpr int kNW16 = 8;   // waves per workgroup of the 16-bit kernel (2 per SIMD)
 
-template <class E, typename OutT, int D>
+template <class E, typename OutT, int D, bool PAGED>
 hipError_t launch16(const FwdParams& p, bool causal, hipStream_t s) {
   if (causal)
-    hipLaunchKernelGGL((fwd16_kernel<E, OutT, D, true, kNW16>), dim3(p.total), dim3(kNW16 * 64),
-                       0, s, p);
+    hipLaunchKernelGGL((fwd16_kernel<E, OutT, D, true, kNW16, PAGED>), dim3(p.total),
+                       dim3(kNW16 * 64), 0, s, p);
   else
-    hipLaunchKernelGGL((fwd16_kernel<E, OutT, D, false, kNW16>), dim3(p.total), dim3(kNW16 * 64),
-                       0, s, p);
+    hipLaunchKernelGGL((fwd16_kernel<E, OutT, D, false, kNW16, PAGED>), dim3(p.total),
+                       dim3(kNW16 * 64), 0, s, p);
   return hipGetLastError();
 }
 
@@ -592,18 +732,49 @@ hipError_t dispatch_d(const FwdParams& p, const ForwardArgs& a, hipStream_t s) {
   const bool c = a.causal != 0;
   switch (a.in_dtype) {
     case FA_BF16:
-      return a.out_dtype == FA_F32 ? launch16<BF16, float, D>(p, c, s)
-                                   : launch16<BF16, __bf16, D>(p, c, s);
+      return a.out_dtype == FA_F32 ? launch16<BF16, float, D, false>(p, c, s)
+                                   : launch16<BF16, __bf16, D, false>(p, c, s);
     case FA_F16:
-      return a.out_dtype == FA_F32 ? launch16<F16, float, D>(p, c, s)
-                                   : launch16<F16, _Float16, D>(p, c, s);
+      return a.out_dtype == FA_F32 ? launch16<F16, float, D, false>(p, c, s)
+                                   : launch16<F16, _Float16, D, false>(p, c, s);
     case FA_F32:
       return launch_t<PolicyF32<D>, float, D>(p, c, s);
   }
   return hipErrorInvalidValue;
 }
 
+template <int D>
+hipError_t dispatch_paged_d(const FwdParams& p, const ForwardPagedArgs& a, hipStream_t s) {
+  const bool c = a.causal != 0;
+  if (a.dtype == FA_BF16)
+    return a.out_dtype == FA_F32 ? launch16<BF16, float, D, true>(p, c, s)
+                                 : launch16<BF16, __bf16, D, true>(p, c, s);
+  return a.out_dtype == FA_F32 ? launch16<F16, float, D, true>(p, c, s)
+                               : launch16<F16, _Float16, D, true>(p, c, s);
+}
+
 }  // namespace
+
+hipError_t launch_forward_paged(const ForwardPagedArgs& a, hipStream_t s) {
+  FwdParams p{};
+  p.q = a.q; p.k = a.k_pool; p.v = a.v_pool; p.o = a.o; p.lse = a.lse;
+  p.B = a.B; p.H = a.H; p.Hkv = a.Hkv;
+  p.group = a.H / a.Hkv;
+  const int br = kNW16 * kQPW;
+  const int max_qb = static_cast<int>((int64_t{a.max_q_len} * p.group + br - 1) / br);
+  p.units = a.causal ? (max_qb + 1) / 2 : max_qb;
+  p.total = (a.B * a.Hkv + kXcds - 1) / kXcds * kXcds * p.units;
+  p.c = a.scale * kLog2e;
+  p.qo_indptr = a.qo_indptr;
+  p.kv_lens = a.kv_lens;
+  p.block_table = a.block_table;
+  p.max_pages = a.max_pages;
+  p.num_pages = a.num_pages;
+  p.total_q = a.total_q;
+  p.max_q_len = a.max_q_len;
+  if (p.total == 0) return hipSuccess;
+  return a.d == 64 ? dispatch_paged_d<64>(p, a, s) : dispatch_paged_d<128>(p, a, s);
+}
 
 hipError_t launch_forward(const ForwardArgs& a, hipStream_t s) {
   FwdParams p;
@@ -611,11 +782,17 @@ hipError_t launch_forward(const ForwardArgs& a, hipStream_t s) {
   p.B = a.B; p.H = a.H; p.Hkv = a.Hkv; p.Nq = a.Nq; p.Nk = a.Nk;
   p.group = a.H / a.Hkv;
   const bool f32 = a.in_dtype == FA_F32;
-  const int br = f32 ? kBR : kNW16 * kQPW;
-  p.n_qblocks = (a.Nq + br - 1) / br;
-  // 16-bit causal: query blocks u and n-1-u share one workgroup.
-  p.units = (!f32 && a.causal) ? (p.n_qblocks + 1) / 2 : p.n_qblocks;
-  p.total = a.B * a.H * p.units;
+  if (f32) {   // one workgroup per (batch, head, 128-row query block)
+    p.n_qblocks = (a.Nq + kBR - 1) / kBR;
+    p.units = p.n_qblocks;
+    p.total = a.B * a.H * p.units;
+  } else {     // per (batch, KV head): blocks of packed (query, head) rows
+    const int br = kNW16 * kQPW;
+    p.n_qblocks = static_cast<int>((int64_t{a.Nq} * p.group + br - 1) / br);
+    // causal: query blocks u and n-1-u share one workgroup
+    p.units = a.causal ? (p.n_qblocks + 1) / 2 : p.n_qblocks;
+    p.total = (a.B * a.Hkv + kXcds - 1) / kXcds * kXcds * p.units;
+  }
   p.c = a.scale * kLog2e;
   p.off = a.Nk - a.Nq;
   if (p.total == 0) return hipSuccess;

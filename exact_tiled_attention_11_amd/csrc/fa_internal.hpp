@@ -42,6 +42,21 @@ struct DecodeArgs {
   int max_splits;   // S
 };
 
+struct ForwardPagedArgs {
+  const void* q;             // [total_q, H, d]
+  const int32_t* qo_indptr;  // [B + 1]
+  const void* k_pool;        // [num_pages, 16, Hkv, d]
+  const void* v_pool;
+  const int32_t* block_table;  // [B, max_pages]
+  const int32_t* kv_lens;      // [B]
+  void* o;                   // [total_q, H, d]
+  float* lse;                // [total_q, H]
+  int B, H, Hkv, d, total_q, max_q_len, max_pages, num_pages;
+  float scale;
+  int causal;
+  fa_dtype dtype, out_dtype;
+};
+
 struct MergeArgs {
   const float* o_parts;
   const float* lse_parts;
@@ -53,6 +68,7 @@ struct MergeArgs {
 };
 
 hipError_t launch_forward(const ForwardArgs& a, hipStream_t s);
+hipError_t launch_forward_paged(const ForwardPagedArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 

@@ -108,6 +108,33 @@ def paged_decode_inputs(B, H, Hkv, d, lens, seed, dtype=torch.bfloat16, page=16,
                        torch.from_numpy(lens.astype(np.int32)), referenced)
 
 
+@dataclass
+class RaggedPagedInputs:
+    q: torch.Tensor             # [total_q, H, d]
+    qo_indptr: torch.Tensor     # [B + 1] int32
+    k_pool: torch.Tensor        # [P, page, Hkv, d]
+    v_pool: torch.Tensor
+    block_table: torch.Tensor   # [B, max_pages] int32, -1 past each sequence's pages
+    kv_lens: torch.Tensor       # [B] int32
+    max_q_len: int
+
+
+def ragged_paged_inputs(q_lens, kv_lens, H, Hkv, d, seed, dtype=torch.bfloat16, page=16,
+                        pool_factor=1.25, unreferenced="nan", q_scale=1.0):
+    """A ragged batch of queries (q_lens[b] rows for sequence b, concatenated)
+    over a shared page pool holding kv_lens[b] tokens per sequence. Pages are
+    taken from one random permutation of the pool; pages no sequence references
+    hold NaN (unreferenced="nan") or N(0,1) values; token slots past a
+    sequence's last token hold N(0,1) values."""
+    q_lens = np.asarray(q_lens, dtype=np.int64)
+    kv = paged_decode_inputs(len(q_lens), H, Hkv, d, kv_lens, seed, dtype, page, pool_factor,
+                             None, unreferenced)
+    indptr = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    q = normal((int(indptr[-1]), H, d), seed * 3 + 3, dtype, q_scale)
+    return RaggedPagedInputs(q, torch.from_numpy(indptr), kv.k_pool, kv.v_pool, kv.block_table,
+                             kv.seq_lens, int(q_lens.max()) if len(q_lens) else 0)
+
+
 def uniform_lengths(B, lo, hi, seed):
     """B integers uniform in [lo, hi] (inclusive)."""
     return np.random.default_rng([seed, 1 << 21]).integers(lo, hi, size=B, endpoint=True)

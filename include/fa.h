@@ -7,6 +7,9 @@
  *                      causal tile skipping ("3.4 Attention Kernels",
  *                      section "FlashAttention: tiling"; "FlashAttention and
  *                      Optimized Kernels", section "The online softmax").
+ *   fa_forward_paged   ragged query batches (prefill chunks and decode tokens of
+ *                      many sequences) over a paged KV cache (section "Paged
+ *                      and ragged layouts: FlashInfer").
  *   fa_decode_paged    one query token per sequence against a paged, ragged
  *                      KV cache, the keys split into chunks whose partial
  *                      results are merged ("3.4 Attention Kernels", sections
@@ -103,6 +106,52 @@ fa_status fa_forward(const void* Q, const void* K, const void* V, void* O,
                      float* LSE, int B, int H, int Hkv, int Nq, int Nk, int d,
                      float scale, int causal, fa_dtype in_dtype,
                      fa_dtype out_dtype, void* stream);
+
+/*
+ * fa_forward_paged - exact attention for ragged query batches over a paged
+ * KV cache: prefill chunks and decode tokens of many sequences in one call.
+ *
+ * "3.4 Attention Kernels", section "Paged and ragged layouts: FlashInfer":
+ * the tokens of all sequences are concatenated without padding and an
+ * offsets array (indptr) marks where each sequence starts; the K/V of each
+ * sequence live in pages found through its block table. Sequence b owns
+ * query rows qo_indptr[b] .. qo_indptr[b+1]-1 of Q and O (q_len_b rows) and
+ * kv_lens[b] cached tokens, token t in page block_table[b*max_pages_per_seq +
+ * t / page_size] at slot t % page_size. Its queries are its NEWEST q_len_b
+ * positions: with causal != 0, its query i (0-based within the sequence)
+ * sees key j iff j <= i + kv_lens[b] - q_len_b (bottom-right alignment, as
+ * fa_forward); a decode step is simply q_len_b = 1. Otherwise as fa_forward:
+ * the same arithmetic, scale, GQA mapping and outputs per (row, head).
+ *
+ * Layouts (row-major, contiguous):
+ *   Q            [total_q, H, d]                      dtype
+ *   qo_indptr    [B + 1]                  int32       device memory
+ *   K_pool,V_pool[num_pages, page_size, Hkv, d]       dtype
+ *   block_table  [B, max_pages_per_seq]   int32       device memory
+ *   kv_lens      [B]                      int32       device memory
+ *   O            [total_q, H, d]                      out_dtype (dtype or FA_F32)
+ *   LSE          [total_q, H]             float
+ *
+ * Supported: dtype in {FA_F16, FA_BF16}; d in {64, 128}; page_size ==
+ * FA_PAGE_SIZE; H % Hkv == 0. max_q_len is an upper bound of every q_len_b
+ * (it sizes the launch); B == 0, total_q == 0 or max_q_len == 0 is a no-op.
+ * Rows of Q/O that belong to no sequence are not touched.
+ * Device-side contract (not checkable on the host without a sync):
+ * 0 <= qo_indptr[b] <= qo_indptr[b+1] <= total_q; q_len_b <= max_q_len;
+ * 0 <= kv_lens[b] <= max_pages_per_seq * page_size; used table entries lie
+ * in [0, num_pages). A sequence with broken indptr entries is skipped (its
+ * rows are unknown); any other violation sets that sequence's O and LSE to
+ * NaN (rows beyond max_q_len may be left unwritten). Nothing is read out of
+ * bounds.
+ */
+fa_status fa_forward_paged(const void* Q, const int32_t* qo_indptr,
+                           const void* K_pool, const void* V_pool,
+                           const int32_t* block_table, const int32_t* kv_lens,
+                           void* O, float* LSE, int B, int H, int Hkv, int d,
+                           int total_q, int max_q_len, int page_size,
+                           int max_pages_per_seq, int num_pages, float scale,
+                           int causal, fa_dtype dtype, fa_dtype out_dtype,
+                           void* stream);
 
 /*
  * fa_decode_num_splits - the number of key chunks fa_decode_paged uses for a

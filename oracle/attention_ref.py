@@ -55,6 +55,7 @@ import numpy as np
 
 __all__ = [
     "attention",
+    "attention_ragged_paged",
     "log_sum_exp",
     "decode_paged",
     "decode_paged_variant",
@@ -287,6 +288,46 @@ def decode_paged(q, k_pool, v_pool, block_table, seq_lens, scale: float):
                                scale, False, np.zeros(1, np.int64), 1)
             out[b, h] = o[0]
             lse[b, h] = l[0]
+    return out, lse
+
+
+def _seq_rows(qo_indptr, b: int):
+    """Query rows of sequence b in a ragged batch: qo_indptr[b] .. qo_indptr[b+1]-1."""
+    return int(qo_indptr[b]), int(qo_indptr[b + 1])
+
+
+def attention_ragged_paged(q, qo_indptr, k_pool, v_pool, block_table, kv_lens, scale: float,
+                           causal: bool, threads: int | None = None):
+    """Attention for a ragged batch of queries over a paged KV cache, by the
+    definition, one sequence at a time.
+
+    "3.4 Attention Kernels", section "Paged and ragged layouts: FlashInfer":
+    the query rows of all sequences are concatenated and `qo_indptr` marks where
+    each sequence starts; each sequence's keys and values are its kv_lens[b]
+    cached tokens, gathered through its block table. The queries of a sequence
+    are its newest positions, so with causal=True the bottom-right alignment of
+    `attention` applies within each sequence (query i sees key j iff
+    j <= i + kv_len - q_len).
+
+    q: [total_q, H, d]; qo_indptr: [B+1]; k_pool, v_pool: [P, page, Hkv, d];
+    block_table: [B, max_pages]; kv_lens: [B]. Returns O [total_q, H, d] and
+    LSE [total_q, H] (float64). Rows of no sequence stay O = 0, LSE = -inf.
+    """
+    q = _f64(q)
+    total_q, H, d = q.shape
+    hkv = k_pool.shape[2]
+    out = np.zeros((total_q, H, d))
+    lse = np.full((total_q, H), -np.inf)
+    for b in range(len(kv_lens)):
+        r0, r1 = _seq_rows(qo_indptr, b)
+        if r1 <= r0:
+            continue
+        L = int(kv_lens[b])
+        kb = gather_paged_kv(k_pool, block_table, L, b) if L else np.zeros((0, hkv, d))
+        vb = gather_paged_kv(v_pool, block_table, L, b) if L else np.zeros((0, hkv, d))
+        o, l = attention(q[r0:r1][None], kb[None], vb[None], scale, causal, threads=threads)
+        out[r0:r1] = o[0]
+        lse[r0:r1] = l[0].T
     return out, lse
 
 

@@ -145,6 +145,33 @@ def test_decode_graph_validation_before_any_hip_call():
     lib.fa_decode_graph_destroy(None)
 
 
+def fwdp(B=2, H=8, Hkv=2, d=128, total_q=10, max_q=8, page=16, max_pages=4, num_pages=8,
+         scale=0.1, causal=1, dt=BF16, outd=BF16, ptrs=(None,) * 8):
+    return fa.lib().fa_forward_paged(*ptrs, B, H, Hkv, d, total_q, max_q, page, max_pages,
+                                     num_pages, scale, causal, dt, outd, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), SHAPE), (dict(H=0), SHAPE), (dict(H=6, Hkv=4), SHAPE),
+    (dict(total_q=-1), SHAPE), (dict(max_q=-1), SHAPE), (dict(max_pages=0), SHAPE),
+    (dict(num_pages=0), SHAPE), (dict(page=0), SHAPE), (dict(dt=7), ARG), (dict(causal=2), ARG),
+    (dict(scale=float("nan")), ARG), (dict(d=96), UNSUP), (dict(page=32), UNSUP),
+    (dict(dt=F32, outd=F32), UNSUP), (dict(dt=F16, outd=BF16), UNSUP),
+    (dict(total_q=1 << 24, H=64), SHAPE), (dict(), NULL), (dict(B=0), OK),
+    (dict(total_q=0), OK), (dict(max_q=0), OK),
+])
+def test_forward_paged_validation(kw, status):
+    assert fwdp(**kw) == status
+
+
+def test_forward_paged_alignment_check():
+    odd = ctypes.c_void_p(0x1002)
+    for i in (0, 2, 3, 6):
+        p = [FAKE] * 8
+        p[i] = odd
+        assert fwdp(ptrs=p) == ARG
+
+
 def test_decode_workspace_checks():
     p = [FAKE] * 7
     need = fa.decode_workspace_size(2, 8, 128, 16)

@@ -408,6 +408,61 @@ def pin_decode_softcap(ref):
             assert abs(l[b, h] - (5.0 + math.log(lens[b]))) < 1e-12
 
 
+def pin_ragged_paged(ref):
+    """Ragged queries over paged K/V == dense attention on each sequence's
+    own contiguous tensors (from which the pools were built), with bottom-right
+    causal alignment when q_len < kv_len; a one-query sequence equals the
+    paged decode; an empty sequence owns no rows; a zero-length cache gives
+    O = 0, LSE = -inf."""
+    rng = np.random.default_rng(33)
+    H, hkv, d, page = 4, 2, 8, 16
+    q_lens = [5, 1, 0, 40, 3]
+    kv_lens = [5, 33, 7, 40, 0]
+    seqs = [(_rand(rng, ql, H, d), _rand(rng, kl, hkv, d), _rand(rng, kl, hkv, d))
+            for ql, kl in zip(q_lens, kv_lens)]
+    B = len(q_lens)
+    indptr = np.concatenate([[0], np.cumsum(q_lens)])
+    q = np.concatenate([sq for sq, _, _ in seqs])
+    need = [-(-kl // page) for kl in kv_lens]
+    n_pages = sum(need) + 4
+    perm = rng.permutation(n_pages)
+    max_pages = max(max(need), 1)
+    table = np.full((B, max_pages), 10**6)
+    kp = _rand(rng, n_pages, page, hkv, d)
+    vp = _rand(rng, n_pages, page, hkv, d)
+    off = 0
+    for b, (_, kk, vv) in enumerate(seqs):
+        for p_ in range(need[b]):
+            pg = perm[off]
+            off += 1
+            table[b, p_] = pg
+            n = min(page, kv_lens[b] - p_ * page)
+            kp[pg, :n] = kk[p_ * page:p_ * page + n]
+            vp[pg, :n] = vv[p_ * page:p_ * page + n]
+    for causal in (False, True):
+        o, l = ref.attention_ragged_paged(q, indptr, kp, vp, table, np.array(kv_lens), 0.35,
+                                          causal)
+        for b, (sq, kk, vv) in enumerate(seqs):
+            r0, r1 = indptr[b], indptr[b + 1]
+            if r1 == r0:
+                continue
+            if kv_lens[b] == 0:
+                assert np.all(o[r0:r1] == 0) and np.all(l[r0:r1] == -np.inf)
+                continue
+            od, ld = ref.attention(sq[None], kk[None], vv[None], 0.35, causal)
+            np.testing.assert_allclose(o[r0:r1], od[0], rtol=0, atol=1e-13)
+            np.testing.assert_allclose(l[r0:r1], ld[0].T, rtol=0, atol=1e-13)
+        # bottom-right: the last query row of sequence 3 sees all 40 keys, its first only key 0
+        r0 = indptr[3]
+        if causal:
+            assert abs(l[r0, 0] - 0.35 * float(seqs[3][0][0, 0] @ seqs[3][1][0, 0])) < 1e-13
+        # the one-query sequence is a decode
+        od, ld = ref.decode_paged(q[indptr[1]:indptr[2]], kp, vp, table[1:2],
+                                  np.array(kv_lens[1:2]), 0.35)
+        np.testing.assert_allclose(o[indptr[1]], od[0], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(l[indptr[1]], ld[0], rtol=0, atol=1e-13)
+
+
 def pin_merge(ref):
     """The merge rule: split partials merged == unsplit, for 1..96 splits
     (more splits than keys gives empty parts); associative; order-free;
@@ -480,7 +535,8 @@ PINS = [pin_lab_example, pin_trace_example, pin_rescale_factor, pin_single_key,
         pin_causal_row0, pin_constant_v, pin_zero_query, pin_rows_sum_to_one,
         pin_brute_force, pin_torch_sdpa, pin_key_permutation,
         pin_gqa_equals_repeated_mha, pin_rows_subset, pin_paged_decode,
-        pin_decode_window, pin_decode_softcap, pin_merge, pin_large_scores]
+        pin_decode_window, pin_decode_softcap, pin_ragged_paged, pin_merge,
+        pin_large_scores]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -624,7 +680,11 @@ def _mut_softcap_no_tanh(m):
     m.setattr(ref_mod, "_soft_cap", lambda x, cap: np.clip(x, -cap, cap))
 
 
-MUTANTS = [_mut_window_off_by_one, _mut_window_oldest, _mut_softcap_unscaled,
+def _mut_ragged_rows_shifted(m):
+    m.setattr(ref_mod, "_seq_rows", lambda ind, b: (int(ind[b]) + (b > 0), int(ind[b + 1])))
+
+
+MUTANTS = [_mut_ragged_rows_shifted, _mut_window_off_by_one, _mut_window_oldest, _mut_softcap_unscaled,
            _mut_softcap_no_tanh, _mut_causal_flipped, _mut_causal_off_by_one, _mut_causal_top_left,
            _mut_no_scale, _mut_transposed_scores, _mut_no_max_subtraction,
            _mut_lse_base2, _mut_lse_without_max, _mut_dropped_sum_term, _mut_gqa_modulo,

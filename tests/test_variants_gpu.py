@@ -188,3 +188,88 @@ def test_decode_graph_replays_match_eager(case):
             assert_lowp_acc("graph", np64(go), ro)
             assert_lse("graph", np64(gl), rl)
     g.close()
+
+
+# ---------------------------------------------------------------------------
+# Ragged queries over a paged cache (fa_forward_paged).
+# ---------------------------------------------------------------------------
+
+def gpu_forward_paged(ri, causal, out_dtype=None, max_q_len=None):
+    say(f"  fa_forward_paged total_q={ri.q.shape[0]} B={ri.kv_lens.shape[0]} causal={causal} "
+        f"out={out_dtype}")
+    o, l = fa.forward_paged(ri.q.to(DEV), ri.qo_indptr.to(DEV), ri.k_pool.to(DEV),
+                            ri.v_pool.to(DEV), ri.block_table.to(DEV), ri.kv_lens.to(DEV),
+                            ri.max_q_len if max_q_len is None else max_q_len, causal=causal,
+                            out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return o, l
+
+
+RAGGED = [
+    # (H, Hkv, d, dtype, q_lens, kv_lens)
+    (8, 2, 128, "bf16", [1, 1, 17, 300, 100, 0, 513, 7, 64],
+     [1, 3000, 17, 300, 2100, 50, 513, 0, 64]),
+    (8, 8, 64, "f16", [33, 1, 256, 257, 5], [33, 4097, 1000, 257, 700]),
+    (32, 8, 128, "bf16", [1000, 1, 1, 2048], [1000, 5000, 1, 2500]),
+]
+
+
+@pytest.mark.parametrize("case", RAGGED, ids=[f"h{c[0]}/{c[1]}-d{c[2]}-{c[3]}-b{len(c[4])}"
+                                             for c in RAGGED])
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_paged_mixed_batch(case, causal):
+    H, Hkv, d, dt, q_lens, kv_lens = case
+    ri = inputs.ragged_paged_inputs(q_lens, kv_lens, H, Hkv, d, seed=51, dtype=TD[dt])
+    # token slots past each sequence's end hold NaN: they must never be used
+    for b, L in enumerate(kv_lens):
+        if L % 16:
+            pg = int(ri.block_table[b, L // 16])
+            ri.k_pool[pg, L % 16:] = float("nan")
+            ri.v_pool[pg, L % 16:] = float("nan")
+    say(f"forward_paged {case} causal={causal}: oracle")
+    ro, rl = oracle.attention_ragged_paged(ri.q, ri.qo_indptr, ri.k_pool, ri.v_pool,
+                                           ri.block_table, ri.kv_lens, 1 / math.sqrt(d), causal)
+    o32, l32 = gpu_forward_paged(ri, causal, torch.float32)
+    o16, l16 = gpu_forward_paged(ri, causal)
+    assert_lowp_acc(f"ragged {case}", np64(o32), ro)
+    assert_lse(f"ragged {case}", np64(l32), rl)
+    assert_rounded_from(f"ragged {case}", o16, o32)
+    assert torch.equal(l16, l32)
+
+
+def test_forward_paged_equals_dense_forward():
+    """Contiguous pages in sequence order hold the dense K/V: the paged kernel
+    gives the dense kernel's results bit for bit."""
+    B, N, H, Hkv, d = 2, 1000, 8, 2, 128
+    q, k, v = inputs.prefill_inputs(B, H, Hkv, N, N, d, torch.bfloat16, seed=52)
+    pages = -(-N // 16)
+    kp = torch.zeros((B * pages, 16, Hkv, d), dtype=torch.bfloat16)
+    vp = torch.zeros_like(kp)
+    kp.view(B, pages * 16, Hkv, d)[:, :N] = k
+    vp.view(B, pages * 16, Hkv, d)[:, :N] = v
+    table = torch.arange(B * pages, dtype=torch.int32).reshape(B, pages)
+    ri = inputs.RaggedPagedInputs(q.reshape(B * N, H, d).contiguous(),
+                                  torch.tensor([0, N, 2 * N], dtype=torch.int32), kp, vp, table,
+                                  torch.tensor([N, N], dtype=torch.int32), N)
+    for causal in (False, True):
+        say(f"forward_paged vs forward causal={causal}")
+        od, ld = fa.forward(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal)
+        op, lp = gpu_forward_paged(ri, causal)
+        assert torch.equal(op.reshape(B, N, H, d), od)
+        assert torch.equal(lp.reshape(B, N, H).permute(0, 2, 1), ld)
+
+
+def test_forward_paged_contract_violations_give_nan():
+    q_lens, kv_lens = [19, 19, 19, 20], [100, 100, 100, 100]
+    ri = inputs.ragged_paged_inputs(q_lens, kv_lens, 8, 2, 128, seed=53)
+    n_pages = ri.k_pool.shape[0]
+    ri.block_table[1, 2] = n_pages          # page id outside the pool
+    ri.kv_lens[2] = 10_000                  # longer than the block table allows
+    say("forward_paged contract violations")
+    for causal in (False, True):
+        # the last sequence is longer than max_q_len = 19
+        o, l = gpu_forward_paged(ri, causal, torch.float32, max_q_len=19)
+        assert torch.isfinite(o[:19]).all() and torch.isfinite(l[:19]).all()
+        for b in (1, 2, 3):
+            r0, r1 = 19 * b, 19 * b + q_lens[b]
+            assert torch.isnan(o[r0:r1]).all() and torch.isnan(l[r0:r1]).all()
