@@ -244,6 +244,56 @@ def bench_forward_paged(torch, fa, inputs, reps=10):
     return out
 
 
+def bench_cascade(torch, fa, inputs, reps=10):
+    """64 decode requests sharing a 16384-token prefix (own suffixes of 16..512
+    tokens): the cascade against the split-KV decode over block tables that
+    list the prefix pages before each request's own pages."""
+    import numpy as np
+    B, H, Hkv, d, P = 64, 32, 8, 128, 16384
+    own = inputs.uniform_lengths(B, 16, 512, 64)
+    ri = inputs.ragged_paged_inputs([1] * B, own, H, Hkv, d, seed=65, pool_factor=1.0,
+                                    unreferenced="normal")
+    n_pre = P // 16
+    pre_k = inputs.normal((n_pre, 16, Hkv, d), 66)
+    pre_v = inputs.normal((n_pre, 16, Hkv, d), 67)
+    base = ri.k_pool.shape[0]
+    kp = torch.cat([ri.k_pool, pre_k]).cuda()
+    vp = torch.cat([ri.v_pool, pre_v]).cuda()
+    prefix_pages = torch.arange(base, base + n_pre, dtype=torch.int32)
+    q, ind = ri.q.cuda(), ri.qo_indptr.cuda()
+    bt, kl = ri.block_table.cuda(), ri.kv_lens.cuda()
+    S = fa.cascade_num_splits(P, B, H, Hkv)
+    ws = torch.empty(fa.cascade_workspace_size(B, H, d, S), dtype=torch.uint8, device="cuda")
+    o = torch.empty((B, H, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    ppd = prefix_pages.cuda()
+
+    def run_cascade():
+        fa.cascade(q, ind, kp, vp, ppd, P, bt, kl, 1, causal=True, out=o, lse=lse, workspace=ws)
+    full = torch.cat([prefix_pages.repeat(B, 1), ri.block_table], dim=1).cuda()
+    full_lens = (ri.kv_lens + P).cuda()
+    dws = torch.empty(fa.decode_workspace_size(B, H, d, fa.MAX_SPLITS), dtype=torch.uint8,
+                      device="cuda")
+    o2 = torch.empty_like(o)
+    l2 = torch.empty_like(lse)
+
+    def run_decode():
+        fa.decode_paged(q, kp, vp, full, full_lens, out=o2, lse=l2, workspace=dws)
+    for _ in range(2):
+        run_cascade()
+        run_decode()
+    t_c = time_steps(torch, run_cascade, reps)
+    t_d = time_steps(torch, run_decode, reps)
+    diff = (o.float() - o2.float()).abs().max().item()
+    kv_row = Hkv * d * 2 * 2
+    return {"workload": "64 decode requests, shared prefix 16384 tokens, own 16..512 tokens, "
+                        "h32/kv8 d128 bf16",
+            "cascade_ms": t_c, "decode_over_full_tables_ms": t_d, "speedup": t_d / t_c,
+            "prefix_splits": S, "max_abs_diff_bf16_out": diff,
+            "kv_bytes_cascade": float(P + int(own.sum())) * kv_row,
+            "kv_bytes_decode": float(B * P + int(own.sum())) * kv_row}
+
+
 def copy_calibration(torch, nbytes=1 << 30, reps=5):
     """A plain device copy of known size, for scaling HBM byte counters."""
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
@@ -261,10 +311,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--parts", default="prefill,decode,variants,graph,paged",
+    ap.add_argument("--parts", default="prefill,decode,variants,graph,paged,cascade",
                     help="comma list: prefill, decode (the timed step), variants (windowed "
                          "and soft-capped decode), graph (graph-replayed decode step), paged "
-                         "(ragged queries over a paged cache)")
+                         "(ragged queries over a paged cache), cascade (shared-prefix decode)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of each oracle baseline sample (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -363,6 +413,9 @@ def main():
     if "paged" in parts:
         log("bench: ragged queries over a paged cache")
         next_rows["forward_paged"] = bench_forward_paged(torch, fa, inputs)
+    if "cascade" in parts:
+        log("bench: cascade over a shared prefix")
+        next_rows["cascade"] = bench_cascade(torch, fa, inputs)
 
     pre_tflops = flops / (pre_ms.mean() * 1e-3) / 1e12 if "prefill" in parts else None
     dec_gbps = kv_bytes / (dec_ms.mean() * 1e-3) / 1e9 if "decode" in parts else None

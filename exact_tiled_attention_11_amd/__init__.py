@@ -35,6 +35,10 @@ _SIGNATURES = {
     "fa_forward": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
     "fa_forward_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I,
                               _I, _F, _I, _I, _I, _P]),
+    "fa_cascade_num_splits": (_I, [_I, _I, _I, _I, _I]),
+    "fa_cascade_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I]),
+    "fa_cascade": (_I, [_P, _P, _P, _P, _P, _I, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I,
+                        _I, _I, _F, _I, _I, _I, _P, ctypes.c_size_t, _P]),
     "fa_decode_num_splits": (_I, [_I, _I]),
     "fa_decode_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "fa_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I,
@@ -163,6 +167,53 @@ def forward_paged(q, qo_indptr, k_pool, v_pool, block_table, kv_lens, max_q_len:
         _code(out_dtype), _stream(q.device))
     _check(st, "fa_forward_paged")
     return out, lse
+
+
+def cascade(q, qo_indptr, k_pool, v_pool, prefix_pages, prefix_len: int, block_table, kv_lens,
+            max_q_len: int, causal: bool = False, prefix_splits: int = 0,
+            scale: float | None = None, out_dtype=None, out=None, lse=None, workspace=None):
+    """Ragged queries over a paged cache whose sequences share one prefix
+    (prefix_pages [ceil(prefix_len/16)] int32), the prefix attended once for all
+    queries. Shapes as forward_paged -> (O [total_q,H,d], LSE [total_q,H])."""
+    if q.dim() != 3 or k_pool.dim() != 4 or v_pool.shape != k_pool.shape:
+        raise ValueError("expected q [total_q,H,d] and pools [P,page,Hkv,d]")
+    total_q, H, d = q.shape
+    num_pages, page, Hkv = k_pool.shape[0], k_pool.shape[1], k_pool.shape[2]
+    B = kv_lens.shape[0]
+    if tuple(qo_indptr.shape) != (B + 1,) or block_table.dim() != 2 or \
+            block_table.shape[0] != B:
+        raise ValueError("qo_indptr must be [B+1] and block_table [B, max_pages]")
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((total_q, H, d), dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((total_q, H), dtype=torch.float32, device=q.device)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    S = cascade_num_splits(prefix_len, total_q, H, Hkv, prefix_splits)
+    if workspace is None and prefix_len > 0 and total_q > 0:
+        workspace = torch.empty(cascade_workspace_size(total_q, H, d, S), dtype=torch.uint8,
+                                device=q.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    pp = _dev(prefix_pages, "prefix_pages", torch.int32) if prefix_pages is not None else None
+    st = lib().fa_cascade(
+        _dev(q, "q"), _dev(qo_indptr, "qo_indptr", torch.int32), _dev(k_pool, "k_pool", q.dtype),
+        _dev(v_pool, "v_pool", q.dtype), pp, int(prefix_len), int(prefix_splits),
+        _dev(block_table, "block_table", torch.int32), _dev(kv_lens, "kv_lens", torch.int32),
+        _dev(out, "out", out_dtype), _dev(lse, "lse", torch.float32), B, H, Hkv, d, total_q,
+        int(max_q_len), page, block_table.shape[1], num_pages, scale, int(bool(causal)),
+        _code(q.dtype), _code(out_dtype), ws_ptr, ws_bytes, _stream(q.device))
+    _check(st, "fa_cascade")
+    return out, lse
+
+
+def cascade_num_splits(prefix_len: int, total_q: int, H: int, Hkv: int,
+                       prefix_splits: int = 0) -> int:
+    return lib().fa_cascade_num_splits(prefix_len, total_q, H, Hkv, prefix_splits)
+
+
+def cascade_workspace_size(total_q: int, H: int, d: int, num_splits: int) -> int:
+    return int(lib().fa_cascade_workspace_size(total_q, H, d, num_splits))
 
 
 def decode_num_splits(seq_len: int, num_splits: int = 0) -> int:

@@ -2,6 +2,7 @@
 // host, then launches on the caller's stream. Nothing here allocates or keeps
 // state; every check runs before the first HIP call so an invalid call has
 // no side effect at all.
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <new>
@@ -102,6 +103,109 @@ fa_status fa_forward_paged(const void* Q, const int32_t* qo_indptr, const void* 
                          B, H, Hkv, d, total_q, max_q_len, max_pages_per_seq, num_pages,
                          scale, causal, dtype, out_dtype};
   return from_hip(fa::launch_forward_paged(a, static_cast<hipStream_t>(stream)));
+}
+
+int fa_cascade_num_splits(int prefix_len, int total_q, int H, int Hkv, int prefix_splits) {
+  if (prefix_len < 0 || total_q < 0 || H < 1 || Hkv < 1 || H % Hkv != 0 || prefix_splits < 0 ||
+      prefix_splits > FA_CASCADE_MAX_SPLITS)
+    return -1;
+  if (prefix_splits > 0) return prefix_splits;
+  // Enough workgroups for two per CU, but at least 512 prefix keys per split.
+  const int64_t blocks = std::max<int64_t>(1, (int64_t{total_q} * (H / Hkv) + 255) / 256);
+  const int64_t want = (512 + int64_t{Hkv} * blocks - 1) / (int64_t{Hkv} * blocks);
+  const int64_t cap = (int64_t{prefix_len} + 511) / 512;
+  return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>({want, cap,
+                                                                  FA_CASCADE_MAX_SPLITS})));
+}
+
+size_t fa_cascade_workspace_size(int total_q, int H, int d, int num_splits) {
+  if (total_q < 0 || H < 1 || d < 1 || num_splits < 1 || num_splits > FA_CASCADE_MAX_SPLITS)
+    return 0;
+  const size_t rows = static_cast<size_t>(total_q) * H;
+  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  return al(rows * num_splits * d * 4) + al(rows * num_splits * 4) + al(rows * d * 4) + rows * 4;
+}
+
+fa_status fa_cascade(const void* Q, const int32_t* qo_indptr, const void* K_pool,
+                     const void* V_pool, const int32_t* prefix_pages, int prefix_len,
+                     int prefix_splits, const int32_t* block_table, const int32_t* kv_lens,
+                     void* O, float* LSE, int B, int H, int Hkv, int d, int total_q,
+                     int max_q_len, int page_size, int max_pages_per_seq, int num_pages,
+                     float scale, int causal, fa_dtype dtype, fa_dtype out_dtype,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  // The suffix pass is exactly fa_forward_paged; validate it first (it
+  // launches nothing on error).
+  if (prefix_len < 0 || prefix_splits < 0 || prefix_splits > FA_CASCADE_MAX_SPLITS)
+    return FA_ERR_BAD_ARG;
+  if (B < 0 || H < 1 || Hkv < 1 || H % Hkv != 0 || total_q < 0 || max_q_len < 0 ||
+      max_pages_per_seq < 1 || num_pages < 1 || page_size < 1)
+    return FA_ERR_BAD_SHAPE;
+  if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return FA_ERR_BAD_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_BAD_ARG;
+  if (!scale_ok(scale)) return FA_ERR_BAD_ARG;
+  if (!head_dim_ok(d) || page_size != FA_PAGE_SIZE || dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  if (out_dtype != dtype && out_dtype != FA_F32) return FA_ERR_UNSUPPORTED;
+  const int S = fa_cascade_num_splits(prefix_len, total_q, H, Hkv, prefix_splits);
+  const int64_t prefix_pages_n = (int64_t{prefix_len} + page_size - 1) / page_size;
+  if (int64_t{total_q} * H * d > kMaxElems || int64_t{total_q} * H * S * d > kMaxElems ||
+      int64_t{num_pages} * page_size * Hkv * d > kMaxElems ||
+      int64_t{B} * max_pages_per_seq > kMaxElems ||
+      int64_t{max_pages_per_seq} * page_size > kMaxElems ||
+      forward16_grid(B, Hkv, H / Hkv, max_q_len, causal != 0) > kMaxElems ||
+      forward16_grid(1, Hkv, H / Hkv, total_q, false) * S > kMaxElems)
+    return FA_ERR_BAD_SHAPE;
+  if (total_q == 0) return FA_OK;
+  if (!Q || !K_pool || !V_pool || !O || !LSE || (prefix_len > 0 && !prefix_pages) ||
+      (B > 0 && (!qo_indptr || !block_table || !kv_lens)))
+    return FA_ERR_NULL_PTR;
+  if (!aligned16(Q) || !aligned16(O) || !aligned16(K_pool) || !aligned16(V_pool))
+    return FA_ERR_BAD_ARG;
+  const size_t need = fa_cascade_workspace_size(total_q, H, d, S);
+  if (prefix_len > 0 && (workspace == nullptr || workspace_bytes < need)) return FA_ERR_WORKSPACE;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+
+  fa::ForwardPagedArgs suf{Q, qo_indptr, K_pool, V_pool, block_table, kv_lens, O, LSE,
+                           B, H, Hkv, d, total_q, max_q_len, max_pages_per_seq, num_pages,
+                           scale, causal, dtype, out_dtype};
+  if (prefix_len == 0) {   // nothing shared: the suffix pass is the answer
+    if (B == 0 || max_q_len == 0) return FA_OK;
+    return from_hip(fa::launch_forward_paged(suf, st));
+  }
+  const size_t rows = static_cast<size_t>(total_q) * H;
+  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  char* w = static_cast<char*>(workspace);
+  float* part_o = reinterpret_cast<float*>(w);
+  float* part_lse = reinterpret_cast<float*>(w + al(rows * S * d * 4));
+  float* suf_o = reinterpret_cast<float*>(w + al(rows * S * d * 4) + al(rows * S * 4));
+  float* suf_lse = reinterpret_cast<float*>(w + al(rows * S * d * 4) + al(rows * S * 4) +
+                                            al(rows * d * 4));
+  // 1. Shared prefix: all query rows against the prefix pages, non-causal,
+  //    split over S key ranges, fp32 partials.
+  fa::ForwardPagedArgs pre{Q, nullptr, K_pool, V_pool, prefix_pages, nullptr, nullptr, nullptr,
+                           1, H, Hkv, d, total_q, total_q,
+                           static_cast<int>(prefix_pages_n), num_pages, scale, 0, dtype,
+                           FA_F32};
+  pre.fixed_kv_len = prefix_len;
+  pre.kv_splits = S;
+  pre.part_o = part_o;
+  pre.part_lse = part_lse;
+  hipError_t e = fa::launch_forward_paged(pre, st);
+  if (e != hipSuccess) return FA_ERR_HIP;
+  // 2. Each sequence's own suffix, fp32.
+  suf.o = suf_o;
+  suf.lse = suf_lse;
+  suf.out_dtype = FA_F32;
+  if (B > 0 && max_q_len > 0) {
+    e = fa::launch_forward_paged(suf, st);
+    if (e != hipSuccess) return FA_ERR_HIP;
+  }
+  // 3. Merge the S prefix parts and the suffix part of every (row, head).
+  fa::MergeArgs m{part_o, part_lse, nullptr, O, LSE, static_cast<int>(rows), S, d, out_dtype};
+  if (B > 0 && max_q_len > 0) {
+    m.o_extra = suf_o;
+    m.lse_extra = suf_lse;
+  }
+  return from_hip(fa::launch_merge(m, st));
 }
 
 int fa_decode_num_splits(int seq_len, int num_splits) {

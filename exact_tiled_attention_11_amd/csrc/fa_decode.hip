@@ -375,6 +375,8 @@ struct MergeParams {
   int fixed_splits;           // decode mode: num_splits argument
   int max_len;                // decode mode: max_pages * page_size
   int window;                 // decode mode: visible-key window (0 = all)
+  const float* o_extra;       // optional part S of every row: [R, d] ...
+  const float* lse_extra;     // ... and [R] (NULL: none)
 };
 
 constexpr int kMergeMaxS = 1024;
@@ -403,6 +405,12 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams a) {
   // in the max.
   float M = kNegInf;
   bool has_nan = false;
+  // The optional extra part: every lane reads it, so it enters the max and
+  // the NaN check once per lane (both idempotent) and its weight is added
+  // after the cross-lane sum.
+  const float le = (!DECODE && a.lse_extra) ? a.lse_extra[r] : kNegInf;
+  has_nan |= le != le;
+  M = fmaxf(M, le);
   for (int c = lane; c < n; c += 64) {
     const float v = lse_r[c];
     has_nan |= v != v;
@@ -427,6 +435,8 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams a) {
   z = sum_xor32(z);
 #pragma unroll
   for (int sh = 16; sh >= 1; sh >>= 1) z += __shfl_xor(z, sh);
+  const float we = le == kNegInf ? 0.f : expf(le - M);   // extra part's weight
+  z += we;
   __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // own wave's LDS writes
   const float inv = 1.f / z;
   for (int x = lane; x < a.d; x += 64) {
@@ -437,6 +447,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams a) {
         if (c < n) acc = fmaf(wsh[wave][c], o_r[c * a.d + x], acc);
     } else {
       for (int c = 0; c < n; ++c) acc = fmaf(wsh[wave][c], o_r[c * a.d + x], acc);
+      if (a.o_extra) acc = fmaf(we, a.o_extra[r * a.d + x], acc);
     }
     store1(out + x, acc * inv);
   }
@@ -526,6 +537,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   m.fixed_splits = a.num_splits;
   m.max_len = a.max_pages * kPage;
   m.window = a.window;
+  m.o_extra = nullptr;
+  m.lse_extra = nullptr;
   return merge_dispatch<true>(m, a.out_dtype, s);
 }
 
@@ -544,6 +557,8 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
   m.fixed_splits = 0;
   m.max_len = 0;
   m.window = 0;
+  m.o_extra = a.o_extra;
+  m.lse_extra = a.lse_extra;
   return merge_dispatch<false>(m, a.out_dtype, s);
 }
 

@@ -57,9 +57,17 @@ struct FwdParams {
   int off;         // Nk - Nq: key j is visible to query i iff j <= i + off
   // Ragged queries over a paged cache (K/V point at the page pools):
   const int32_t* qo_indptr;    // [B + 1]: rows of sequence b are qo_indptr[b] ..
-  const int32_t* kv_lens;      // [B]
+                               //   (NULL: one sequence owning all total_q rows)
+  const int32_t* kv_lens;      // [B] (NULL: every sequence has fixed_kv_len keys)
   const int32_t* block_table;  // [B, max_pages]
-  int max_pages, num_pages, total_q, max_q_len;
+  int max_pages, num_pages, total_q, max_q_len, fixed_kv_len;
+  // Partial mode (non-causal, part_o != NULL): each query block is processed
+  // by kv_splits workgroups over near-equal key-tile ranges, each writing an
+  // fp32 partial (o, lse) to part_o [total_q * H, kv_splits, D] and
+  // part_lse [total_q * H, kv_splits] instead of O and LSE.
+  int kv_splits;
+  float* part_o;
+  float* part_lse;
 };
 
 // ---------------------------------------------------------------------------
@@ -215,11 +223,12 @@ void fwd16_kernel(const FwdParams a) {
   int64_t q_row0;
   bool bad = false;   // device-side contract violation: this sequence's outputs are NaN
   if constexpr (PAGED) {
-    const int qs = a.qo_indptr[b], qe = a.qo_indptr[b + 1];
+    const int qs = a.qo_indptr ? a.qo_indptr[b] : 0;
+    const int qe = a.qo_indptr ? a.qo_indptr[b + 1] : a.total_q;
     if (qs < 0 || qe < qs || qe > a.total_q) return;   // rows unknown: nothing is written
     Nq = qe - qs;
     q_row0 = qs;
-    Nk = a.kv_lens[b];
+    Nk = a.kv_lens ? a.kv_lens[b] : a.fixed_kv_len;
     if (Nk < 0 || Nk > a.max_pages * kPageTokens || Nq > a.max_q_len) {
       bad = true;
       Nk = 0;
@@ -232,22 +241,34 @@ void fwd16_kernel(const FwdParams a) {
   const int nrows = Nq * G;   // packed rows of this (sequence, KV head)
   nqb = (nrows + BR - 1) / BR;
   const int off = Nk - Nq;
-  if (u >= (CAUSAL ? (nqb + 1) / 2 : nqb)) return;   // whole workgroup: uniform
+  // Partial mode (paged, non-causal, part_o set): unit = query unit *
+  // kv_splits + split, and each split writes an fp32 partial (o, lse).
+  const bool partial = PAGED && !CAUSAL && a.part_o != nullptr;
+  const int S = partial ? a.kv_splits : 1;
+  const int uq = S > 1 ? u / S : u;
+  const int split = u - uq * S;
+  if (uq >= (CAUSAL ? (nqb + 1) / 2 : nqb)) return;   // whole workgroup: uniform
 
-  const int qb_first = u;
-  const int qb_second = CAUSAL ? nqb - 1 - u : u;
+  const int qb_first = uq;
+  const int qb_second = CAUSAL ? nqb - 1 - uq : uq;
   const int nseg = (CAUSAL && qb_second > qb_first) ? 2 : 1;
   auto block_tiles = [&](int qb) {
     int last = Nk - 1;
     if (CAUSAL) last = min(last, min(qb * BR + BR, nrows) / G - 1 + off);
     return tile_count(last);
   };
-  const int n0 = block_tiles(qb_first);
+  int n0 = block_tiles(qb_first);
+  int t_begin = 0;   // first key tile of this split
+  if (S > 1) {       // near-equal tile ranges, the first n0 % S one tile longer
+    const int q = n0 / S, r = n0 % S;
+    t_begin = split * q + min(split, r);
+    n0 = q + (split < r ? 1 : 0);
+  }
   const int n1 = nseg == 2 ? block_tiles(qb_second) : 0;
   const int n_steps = n0 + n1;
   // Key tile streamed at step g: ascending through the first block, then
   // descending through the second.
-  auto tile_at = [&](int g) { return g < n0 ? g : n_steps - 1 - g; };
+  auto tile_at = [&](int g) { return g < n0 ? t_begin + g : n_steps - 1 - g; };
 
   const int64_t q_rs = static_cast<int64_t>(a.H) * D;
   const int64_t kv_rs = static_cast<int64_t>(a.Hkv) * D;
@@ -350,7 +371,7 @@ void fwd16_kernel(const FwdParams a) {
     float m_run = kNegInf, m2_run = kNegInf, l_run = 0.f;   // this lane's query row
 
     for (int j = 0; j < nt; ++j, ++g) {
-      const int k0 = (seg == 0 ? j : nt - 1 - j) * kBC;
+      const int k0 = tile_at(g) * kBC;
       const bool more = g + ST - 1 < n_steps;
       if (more) {
         if constexpr (PAGED) {
@@ -477,7 +498,20 @@ void fwd16_kernel(const FwdParams a) {
       inv = __builtin_nanf("");
       lse_v = __builtin_nanf("");
     }
-    if (qrow < Nq) {
+    if (partial) {   // key split: fp32 partial (o, lse) of this split
+      if (qrow < Nq) {
+        const int64_t pr = ((q_row0 + qrow) * a.H + h) * S + split;
+        float* prow = a.part_o + pr * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int gg = 0; gg < 4; ++gg)
+            store4(prow + 32 * db + 8 * gg + 4 * khi, acc[db][4 * gg] * inv,
+                   acc[db][4 * gg + 1] * inv, acc[db][4 * gg + 2] * inv,
+                   acc[db][4 * gg + 3] * inv);
+        if (lane < 32) a.part_lse[pr] = lse_v;
+      }
+    } else if (qrow < Nq) {
       OutT* orow = static_cast<OutT*>(a.o) + (q_row0 + qrow) * q_rs +
                    static_cast<int64_t>(h) * D;
 #pragma unroll
@@ -762,7 +796,12 @@ hipError_t launch_forward_paged(const ForwardPagedArgs& a, hipStream_t s) {
   p.group = a.H / a.Hkv;
   const int br = kNW16 * kQPW;
   const int max_qb = static_cast<int>((int64_t{a.max_q_len} * p.group + br - 1) / br);
-  p.units = a.causal ? (max_qb + 1) / 2 : max_qb;
+  const bool partial = !a.causal && a.part_o != nullptr;
+  p.kv_splits = partial ? a.kv_splits : 1;
+  p.units = a.causal ? (max_qb + 1) / 2 : max_qb * p.kv_splits;
+  p.fixed_kv_len = a.fixed_kv_len;
+  p.part_o = a.part_o;
+  p.part_lse = a.part_lse;
   p.total = (a.B * a.Hkv + kXcds - 1) / kXcds * kXcds * p.units;
   p.c = a.scale * kLog2e;
   p.qo_indptr = a.qo_indptr;
@@ -777,7 +816,8 @@ hipError_t launch_forward_paged(const ForwardPagedArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_forward(const ForwardArgs& a, hipStream_t s) {
-  FwdParams p;
+  FwdParams p{};
+  p.kv_splits = 1;
   p.q = a.q; p.k = a.k; p.v = a.v; p.o = a.o; p.lse = a.lse;
   p.B = a.B; p.H = a.H; p.Hkv = a.Hkv; p.Nq = a.Nq; p.Nk = a.Nk;
   p.group = a.H / a.Hkv;

@@ -55,6 +55,13 @@ struct ForwardPagedArgs {
   float scale;
   int causal;
   fa_dtype dtype, out_dtype;
+  // qo_indptr / kv_lens may be NULL: one sequence of all total_q rows /
+  // fixed_kv_len keys per sequence.
+  int fixed_kv_len = 0;
+  // kv_splits > 1 (non-causal only): write fp32 partials instead of O, LSE.
+  int kv_splits = 1;
+  float* part_o = nullptr;    // [total_q * H, kv_splits, d]
+  float* part_lse = nullptr;  // [total_q * H, kv_splits]
 };
 
 struct MergeArgs {
@@ -65,6 +72,8 @@ struct MergeArgs {
   float* lse;
   int R, S, d;
   fa_dtype out_dtype;
+  const float* o_extra = nullptr;    // optional extra part per row: [R, d]
+  const float* lse_extra = nullptr;  // [R]
 };
 
 hipError_t launch_forward(const ForwardArgs& a, hipStream_t s);

@@ -10,6 +10,10 @@
  *   fa_forward_paged   ragged query batches (prefill chunks and decode tokens of
  *                      many sequences) over a paged KV cache (section "Paged
  *                      and ragged layouts: FlashInfer").
+ *   fa_cascade         the same for sequences sharing one prefix, whose
+ *                      attention is computed once for all queries and merged
+ *                      with each sequence's own suffix (cascade attention,
+ *                      same section).
  *   fa_decode_paged    one query token per sequence against a paged, ragged
  *                      KV cache, the keys split into chunks whose partial
  *                      results are merged ("3.4 Attention Kernels", sections
@@ -71,6 +75,8 @@ typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
 #define FA_MAX_SPLITS 16
 /* Token slots per KV page accepted by fa_decode_paged. */
 #define FA_PAGE_SIZE 16
+/* Largest number of key ranges fa_cascade splits the shared prefix into. */
+#define FA_CASCADE_MAX_SPLITS 64
 
 /*
  * fa_forward - exact attention forward for dense batched tensors.
@@ -152,6 +158,52 @@ fa_status fa_forward_paged(const void* Q, const int32_t* qo_indptr,
                            int max_pages_per_seq, int num_pages, float scale,
                            int causal, fa_dtype dtype, fa_dtype out_dtype,
                            void* stream);
+
+/*
+ * fa_cascade - fa_forward_paged for sequences that all start with one shared
+ * prefix, with the prefix's attention computed once for every query.
+ *
+ * "3.4 Attention Kernels", section "Paged and ragged layouts: FlashInfer"
+ * (cascade attention): when requests share a prefix, attention over that
+ * prefix is computed once for all of their queries and merged with each
+ * request's own-suffix attention by the merge rule of section "Online
+ * softmax". Sequence b's keys are the prefix_len prefix tokens (token t in
+ * page prefix_pages[t / page_size], slot t % page_size, of the same pools)
+ * followed by its own kv_lens[b] tokens (block_table, as fa_forward_paged).
+ * Its q_len_b queries are its newest positions; with causal != 0 they see the
+ * whole prefix and the suffix keys j <= i + kv_lens[b] - q_len_b. The result
+ * equals attention over the concatenated keys, provided every query lies in
+ * its own suffix (q_len_b <= kv_lens[b] when causal).
+ *
+ * The work: (1) all total_q query rows against the prefix, non-causal, the
+ * prefix cut into S = fa_cascade_num_splits(prefix_len, total_q, H, Hkv,
+ * prefix_splits) near-equal key ranges, each giving an fp32 partial (o, lse)
+ * per (row, head); (2) every sequence's own suffix as fa_forward_paged, in
+ * fp32; (3) the merge of the S + 1 parts of every (row, head) into O and LSE.
+ * With prefix_len == 0 it is exactly fa_forward_paged.
+ *
+ * Layouts and support: as fa_forward_paged (Q, O [total_q, H, d]; LSE
+ * [total_q, H]), plus prefix_pages [ceil(prefix_len / page_size)] int32 in
+ * device memory and a device workspace of at least
+ * fa_cascade_workspace_size(total_q, H, d, S) bytes when prefix_len > 0
+ * (contents on entry ignored, on exit unspecified). 0 <= prefix_splits <=
+ * FA_CASCADE_MAX_SPLITS (0 = automatic). Device-side contract: as
+ * fa_forward_paged, plus qo_indptr[0] == 0 and qo_indptr[B] == total_q (rows
+ * outside every sequence get unspecified output) and prefix page ids in
+ * [0, num_pages); violations give NaN rows instead of out-of-bounds reads.
+ */
+int fa_cascade_num_splits(int prefix_len, int total_q, int H, int Hkv,
+                          int prefix_splits);
+size_t fa_cascade_workspace_size(int total_q, int H, int d, int num_splits);
+fa_status fa_cascade(const void* Q, const int32_t* qo_indptr,
+                     const void* K_pool, const void* V_pool,
+                     const int32_t* prefix_pages, int prefix_len,
+                     int prefix_splits, const int32_t* block_table,
+                     const int32_t* kv_lens, void* O, float* LSE, int B, int H,
+                     int Hkv, int d, int total_q, int max_q_len, int page_size,
+                     int max_pages_per_seq, int num_pages, float scale,
+                     int causal, fa_dtype dtype, fa_dtype out_dtype,
+                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * fa_decode_num_splits - the number of key chunks fa_decode_paged uses for a

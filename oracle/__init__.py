@@ -8,6 +8,7 @@ passages of the pages each function follows.
 from .attention_ref import (  # noqa: F401
     attention,
     attention_ragged_paged,
+    cascade_attention,
     causal_visible,
     decode_paged,
     decode_paged_variant,

@@ -56,6 +56,7 @@ import numpy as np
 __all__ = [
     "attention",
     "attention_ragged_paged",
+    "cascade_attention",
     "log_sum_exp",
     "decode_paged",
     "decode_paged_variant",
@@ -326,6 +327,46 @@ def attention_ragged_paged(q, qo_indptr, k_pool, v_pool, block_table, kv_lens, s
         kb = gather_paged_kv(k_pool, block_table, L, b) if L else np.zeros((0, hkv, d))
         vb = gather_paged_kv(v_pool, block_table, L, b) if L else np.zeros((0, hkv, d))
         o, l = attention(q[r0:r1][None], kb[None], vb[None], scale, causal, threads=threads)
+        out[r0:r1] = o[0]
+        lse[r0:r1] = l[0].T
+    return out, lse
+
+
+def _concat_keys(prefix: np.ndarray, own: np.ndarray) -> np.ndarray:
+    """A sequence's keys (or values) in a cascade: the shared prefix first."""
+    return np.concatenate([prefix, own], axis=0)
+
+
+def cascade_attention(q, qo_indptr, k_pool, v_pool, prefix_pages, prefix_len: int,
+                      block_table, kv_lens, scale: float, causal: bool,
+                      threads: int | None = None):
+    """Attention for sequences sharing one prefix, by the definition.
+
+    "3.4 Attention Kernels", section "Paged and ragged layouts: FlashInfer"
+    (cascade attention): sequence b's keys and values are the prefix_len
+    shared prefix tokens (token t in page prefix_pages[t // page], slot
+    t % page) followed by its own kv_lens[b] tokens from its block table. The
+    result is plain attention over that concatenation, bottom-right causal
+    when causal=True, i.e. what the cascade's merge of prefix and suffix parts
+    must reproduce. Shapes and outputs as `attention_ragged_paged`.
+    """
+    q = _f64(q)
+    total_q, H, d = q.shape
+    hkv = k_pool.shape[2]
+    table = np.asarray(prefix_pages).reshape(1, -1)
+    pk = gather_paged_kv(k_pool, table, prefix_len, 0) if prefix_len else np.zeros((0, hkv, d))
+    pv = gather_paged_kv(v_pool, table, prefix_len, 0) if prefix_len else np.zeros((0, hkv, d))
+    out = np.zeros((total_q, H, d))
+    lse = np.full((total_q, H), -np.inf)
+    for b in range(len(kv_lens)):
+        r0, r1 = _seq_rows(qo_indptr, b)
+        if r1 <= r0:
+            continue
+        L = int(kv_lens[b])
+        kb = gather_paged_kv(k_pool, block_table, L, b) if L else np.zeros((0, hkv, d))
+        vb = gather_paged_kv(v_pool, block_table, L, b) if L else np.zeros((0, hkv, d))
+        kk, vv = _concat_keys(pk, kb), _concat_keys(pv, vb)
+        o, l = attention(q[r0:r1][None], kk[None], vv[None], scale, causal, threads=threads)
         out[r0:r1] = o[0]
         lse[r0:r1] = l[0].T
     return out, lse

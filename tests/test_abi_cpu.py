@@ -172,6 +172,61 @@ def test_forward_paged_alignment_check():
         assert fwdp(ptrs=p) == ARG
 
 
+def casc(prefix_len=100, prefix_splits=0, B=2, H=8, Hkv=2, d=128, total_q=10, max_q=8, page=16,
+         max_pages=4, num_pages=8, scale=0.1, causal=1, dt=BF16, outd=BF16, ptrs=(None,) * 8,
+         ws=None, ws_bytes=0):
+    q, ind, k, v, pp, bt, kl, o = ptrs
+    return fa.lib().fa_cascade(q, ind, k, v, pp, prefix_len, prefix_splits, bt, kl, o, None,
+                               B, H, Hkv, d, total_q, max_q, page, max_pages, num_pages, scale,
+                               causal, dt, outd, ws, ws_bytes, None)
+
+
+def test_cascade_split_rule_and_workspace():
+    # explicit count wins; automatic: enough workgroups, at least 512 prefix keys each, <= 64
+    assert fa.cascade_num_splits(10000, 64, 32, 8, 5) == 5
+    assert fa.cascade_num_splits(100, 64, 32, 8, 0) == 1
+    assert fa.cascade_num_splits(16384, 64, 32, 8, 0) == 32
+    assert fa.cascade_num_splits(10**6, 64, 32, 8, 0) == 64
+    assert fa.cascade_num_splits(10**6, 65536, 32, 8, 0) == 1
+    assert fa.cascade_num_splits(0, 64, 32, 8, 0) == 1
+    assert fa.cascade_num_splits(-1, 64, 32, 8, 0) == -1
+    assert fa.cascade_num_splits(100, 64, 32, 8, 65) == -1
+    assert fa.cascade_num_splits(100, 64, 32, 6, 0) == -1
+    ws = fa.cascade_workspace_size(10, 8, 128, 4)
+    rows = 80
+    assert ws == (rows * 4 * 128 * 4) + -(-rows * 4 * 4 // 256) * 256 + rows * 128 * 4 + rows * 4
+    assert fa.cascade_workspace_size(10, 8, 128, 0) == 0
+    assert fa.cascade_workspace_size(10, 8, 128, 65) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(prefix_len=-1), ARG), (dict(prefix_splits=-1), ARG), (dict(prefix_splits=65), ARG),
+    (dict(B=-1), SHAPE), (dict(H=6, Hkv=4), SHAPE), (dict(total_q=-1), SHAPE), (dict(dt=7), ARG),
+    (dict(causal=3), ARG), (dict(scale=0.0), ARG), (dict(d=80), UNSUP), (dict(page=8), UNSUP),
+    (dict(dt=F32, outd=F32), UNSUP), (dict(total_q=0), OK), (dict(), NULL),
+])
+def test_cascade_validation(kw, status):
+    assert casc(**kw) == status
+
+
+def test_cascade_pointer_and_workspace_checks():
+    p = [FAKE] * 8
+    assert casc(ptrs=p) == NULL   # LSE is NULL in every call of this helper
+    need = fa.cascade_workspace_size(10, 8, 128, fa.cascade_num_splits(100, 10, 8, 2, 0))
+    lib = fa.lib()
+
+    def call(prefix_len, ws, ws_bytes, pp=FAKE):
+        return lib.fa_cascade(FAKE, FAKE, FAKE, FAKE, pp, prefix_len, 0, FAKE, FAKE, FAKE, FAKE,
+                              2, 8, 2, 128, 10, 8, 16, 4, 8, 0.1, 1, BF16, BF16, ws, ws_bytes,
+                              None)
+    assert call(100, None, 0) == WS
+    assert call(100, FAKE, need - 1) == WS
+    assert call(100, FAKE, need, pp=None) == NULL
+    odd = ctypes.c_void_p(0x1002)
+    assert lib.fa_cascade(odd, FAKE, FAKE, FAKE, FAKE, 100, 0, FAKE, FAKE, FAKE, FAKE, 2, 8, 2,
+                          128, 10, 8, 16, 4, 8, 0.1, 1, BF16, BF16, FAKE, need, None) == ARG
+
+
 def test_decode_workspace_checks():
     p = [FAKE] * 7
     need = fa.decode_workspace_size(2, 8, 128, 16)

@@ -463,6 +463,66 @@ def pin_ragged_paged(ref):
         np.testing.assert_allclose(l[indptr[1]], ld[0], rtol=0, atol=1e-13)
 
 
+def pin_cascade(ref):
+    """Cascade: dense attention over [prefix ++ own tokens] built from the
+    original contiguous tensors; equal to the ragged paged attention with the
+    (page-aligned) prefix pages prepended to each block table; equal to the
+    merge of the prefix-only (non-causal) and suffix-only parts; prefix 0 is
+    the plain ragged attention."""
+    rng = np.random.default_rng(34)
+    H, hkv, d, page = 4, 2, 8, 16
+    P = 32                      # page-aligned shared prefix
+    q_lens, kv_lens = [3, 1, 6, 0], [5, 20, 6, 4]
+    B = len(q_lens)
+    pk, pv = _rand(rng, P, hkv, d), _rand(rng, P, hkv, d)
+    own = [(_rand(rng, ql, H, d), _rand(rng, kl, hkv, d), _rand(rng, kl, hkv, d))
+           for ql, kl in zip(q_lens, kv_lens)]
+    n_pages = P // page + sum(-(-kl // page) for kl in kv_lens) + 2
+    perm = rng.permutation(n_pages)
+    kp, vp = _rand(rng, n_pages, page, hkv, d), _rand(rng, n_pages, page, hkv, d)
+    prefix_pages = perm[:P // page]
+    for i, pg in enumerate(prefix_pages):
+        kp[pg], vp[pg] = pk[i * page:(i + 1) * page], pv[i * page:(i + 1) * page]
+    max_pages = max(-(-kl // page) for kl in kv_lens)
+    table = np.full((B, max_pages), 10**6)
+    nxt = P // page
+    for b, (_, kk, vv) in enumerate(own):
+        for p_ in range(-(-kv_lens[b] // page)):
+            pg = perm[nxt]
+            nxt += 1
+            table[b, p_] = pg
+            n = min(page, kv_lens[b] - p_ * page)
+            kp[pg, :n], vp[pg, :n] = kk[p_ * page:p_ * page + n], vv[p_ * page:p_ * page + n]
+    indptr = np.concatenate([[0], np.cumsum(q_lens)])
+    q = np.concatenate([x for x, _, _ in own])
+    lens = np.array(kv_lens)
+    for causal in (False, True):
+        o, l = ref.cascade_attention(q, indptr, kp, vp, prefix_pages, P, table, lens, 0.3, causal)
+        for b, (sq, kk, vv) in enumerate(own):
+            if q_lens[b] == 0:
+                continue
+            od, ld = ref.attention(sq[None], np.concatenate([pk, kk])[None],
+                                   np.concatenate([pv, vv])[None], 0.3, causal)
+            np.testing.assert_allclose(o[indptr[b]:indptr[b + 1]], od[0], rtol=0, atol=1e-13)
+            np.testing.assert_allclose(l[indptr[b]:indptr[b + 1]], ld[0].T, rtol=0, atol=1e-13)
+        full = np.concatenate([np.tile(prefix_pages, (B, 1)), table], axis=1)
+        o2, l2 = ref.attention_ragged_paged(q, indptr, kp, vp, full, lens + P, 0.3, causal)
+        np.testing.assert_allclose(o2, o, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(l2, l, rtol=0, atol=1e-13)
+        op, lp = ref.attention_ragged_paged(q, np.array([0, len(q)]), kp, vp,
+                                            prefix_pages[None], np.array([P]), 0.3, False)
+        os_, ls_ = ref.attention_ragged_paged(q, indptr, kp, vp, table, lens, 0.3, causal)
+        R = len(q) * H
+        om, lm = ref.merge_partials(np.stack([op.reshape(R, d), os_.reshape(R, d)], axis=1),
+                                    np.stack([lp.reshape(R), ls_.reshape(R)], axis=1))
+        np.testing.assert_allclose(om.reshape(o.shape), o, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(lm.reshape(l.shape), l, rtol=0, atol=1e-13)
+        o0, l0 = ref.cascade_attention(q, indptr, kp, vp, prefix_pages[:0], 0, table, lens, 0.3,
+                                       causal)
+        np.testing.assert_allclose(o0, os_, rtol=0, atol=1e-14)
+        np.testing.assert_allclose(l0, ls_, rtol=0, atol=1e-14)
+
+
 def pin_merge(ref):
     """The merge rule: split partials merged == unsplit, for 1..96 splits
     (more splits than keys gives empty parts); associative; order-free;
@@ -535,7 +595,7 @@ PINS = [pin_lab_example, pin_trace_example, pin_rescale_factor, pin_single_key,
         pin_causal_row0, pin_constant_v, pin_zero_query, pin_rows_sum_to_one,
         pin_brute_force, pin_torch_sdpa, pin_key_permutation,
         pin_gqa_equals_repeated_mha, pin_rows_subset, pin_paged_decode,
-        pin_decode_window, pin_decode_softcap, pin_ragged_paged, pin_merge,
+        pin_decode_window, pin_decode_softcap, pin_ragged_paged, pin_cascade, pin_merge,
         pin_large_scores]
 
 
@@ -684,7 +744,11 @@ def _mut_ragged_rows_shifted(m):
     m.setattr(ref_mod, "_seq_rows", lambda ind, b: (int(ind[b]) + (b > 0), int(ind[b + 1])))
 
 
-MUTANTS = [_mut_ragged_rows_shifted, _mut_window_off_by_one, _mut_window_oldest, _mut_softcap_unscaled,
+def _mut_cascade_prefix_last(m):
+    m.setattr(ref_mod, "_concat_keys", lambda prefix, own: np.concatenate([own, prefix], axis=0))
+
+
+MUTANTS = [_mut_cascade_prefix_last, _mut_ragged_rows_shifted, _mut_window_off_by_one, _mut_window_oldest, _mut_softcap_unscaled,
            _mut_softcap_no_tanh, _mut_causal_flipped, _mut_causal_off_by_one, _mut_causal_top_left,
            _mut_no_scale, _mut_transposed_scores, _mut_no_max_subtraction,
            _mut_lse_base2, _mut_lse_without_max, _mut_dropped_sum_term, _mut_gqa_modulo,

@@ -273,3 +273,85 @@ def test_forward_paged_contract_violations_give_nan():
         for b in (1, 2, 3):
             r0, r1 = 19 * b, 19 * b + q_lens[b]
             assert torch.isnan(o[r0:r1]).all() and torch.isnan(l[r0:r1]).all()
+
+
+# ---------------------------------------------------------------------------
+# Cascade: a shared prefix attended once, merged with each sequence's suffix.
+# ---------------------------------------------------------------------------
+
+def cascade_case(prefix_len, q_lens, kv_lens, H, Hkv, d, dt, seed):
+    """Ragged inputs whose pool also holds a shared prefix of prefix_len tokens
+    in pages of its own; token slots after the prefix's last token hold NaN."""
+    ri = inputs.ragged_paged_inputs(q_lens, kv_lens, H, Hkv, d, seed=seed, dtype=TD[dt],
+                                    unreferenced="nan")
+    n_pre = -(-prefix_len // 16)
+    extra = inputs.normal((n_pre, 16, Hkv, d), seed * 7 + 1, TD[dt])
+    extra_v = inputs.normal((n_pre, 16, Hkv, d), seed * 7 + 2, TD[dt])
+    perm = np.random.default_rng(seed).permutation(n_pre)
+    if prefix_len % 16:   # the page holding the prefix's last token
+        extra[perm[-1], prefix_len % 16:] = float("nan")
+        extra_v[perm[-1], prefix_len % 16:] = float("nan")
+    base = ri.k_pool.shape[0]
+    ri.k_pool = torch.cat([ri.k_pool, extra])
+    ri.v_pool = torch.cat([ri.v_pool, extra_v])
+    prefix_pages = torch.from_numpy((base + perm).astype(np.int32))
+    for b, L in enumerate(kv_lens):
+        if L % 16:
+            pg = int(ri.block_table[b, L // 16])
+            ri.k_pool[pg, L % 16:] = float("nan")
+            ri.v_pool[pg, L % 16:] = float("nan")
+    return ri, prefix_pages
+
+
+def gpu_cascade(ri, prefix_pages, prefix_len, causal, splits=0, out_dtype=None):
+    say(f"  fa_cascade total_q={ri.q.shape[0]} prefix={prefix_len} splits={splits} "
+        f"causal={causal} out={out_dtype}")
+    o, l = fa.cascade(ri.q.to(DEV), ri.qo_indptr.to(DEV), ri.k_pool.to(DEV), ri.v_pool.to(DEV),
+                      prefix_pages.to(DEV), prefix_len, ri.block_table.to(DEV),
+                      ri.kv_lens.to(DEV), ri.max_q_len, causal=causal, prefix_splits=splits,
+                      out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return o, l
+
+
+CASCADE = [
+    # (prefix_len, H, Hkv, d, dtype, q_lens, kv_lens)
+    (16, 8, 2, 128, "bf16", [1, 1, 5, 40], [1, 300, 5, 100]),
+    (1000, 8, 8, 64, "f16", [1, 17, 1, 0], [2049, 17, 60, 9]),
+    (5000, 32, 8, 128, "bf16", [1] * 12 + [300], [100 * (i + 1) for i in range(12)] + [300]),
+]
+
+
+@pytest.mark.parametrize("case", CASCADE, ids=[f"p{c[0]}-h{c[1]}/{c[2]}-d{c[3]}-{c[4]}"
+                                              for c in CASCADE])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("splits", [0, 1, 7])
+def test_cascade(case, causal, splits):
+    P, H, Hkv, d, dt, q_lens, kv_lens = case
+    ri, pp = cascade_case(P, q_lens, kv_lens, H, Hkv, d, dt, seed=71)
+    say(f"cascade {case} causal={causal} splits={splits}: oracle")
+    ro, rl = oracle.cascade_attention(ri.q, ri.qo_indptr, ri.k_pool, ri.v_pool, pp, P,
+                                      ri.block_table, ri.kv_lens, 1 / math.sqrt(d), causal)
+    o32, l32 = gpu_cascade(ri, pp, P, causal, splits, torch.float32)
+    o16, l16 = gpu_cascade(ri, pp, P, causal, splits)
+    assert_lowp_acc(f"cascade {case}", np64(o32), ro)
+    assert_lse(f"cascade {case}", np64(l32), rl)
+    assert_rounded_from(f"cascade {case}", o16, o32)
+    assert torch.equal(l16, l32)
+
+
+def test_cascade_without_prefix_is_forward_paged():
+    ri, pp = cascade_case(0, [1, 7, 300], [500, 7, 300], 8, 2, 128, "bf16", seed=72)
+    for causal in (False, True):
+        say(f"cascade prefix 0 vs forward_paged causal={causal}")
+        a = gpu_cascade(ri, pp, 0, causal)
+        b = gpu_forward_paged(ri, causal)
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_cascade_bad_prefix_page_gives_nan():
+    ri, pp = cascade_case(64, [1, 3], [40, 40], 8, 2, 128, "bf16", seed=73)
+    pp[1] = ri.k_pool.shape[0] + 3           # outside the pool
+    say("cascade bad prefix page")
+    o, l = gpu_cascade(ri, pp, 64, True, 0, torch.float32)
+    assert torch.isnan(o).all() and torch.isnan(l).all()
