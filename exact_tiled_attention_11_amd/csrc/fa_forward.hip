@@ -3,8 +3,9 @@
 //
 // The method is the one of "3.4 Attention Kernels", section "FlashAttention:
 // tiling" (also "FlashAttention and Optimized Kernels", section "The online
-// softmax"): for a block of query rows keep a running max m, running sum l and
-// unnormalised output acc; for each key tile compute the score tile, raise m,
+// softmax"): each query row carries its largest score so far m, the sum l of
+// its exponentials and the unnormalised output acc; per key tile compute the
+// score tile, raise m,
 // rescale l and acc by e^(m_old - m_new), add the tile's contribution; write
 // O = acc / l and LSE = m + ln l once at the end (normalising once, as
 // section "FlashAttention-2 and -3" describes). Key tiles wholly above the

@@ -164,9 +164,10 @@ fa_status fa_forward_paged(const void* Q, const int32_t* qo_indptr,
  * prefix, with the prefix's attention computed once for every query.
  *
  * "3.4 Attention Kernels", section "Paged and ragged layouts: FlashInfer"
- * (cascade attention): when requests share a prefix, attention over that
- * prefix is computed once for all of their queries and merged with each
- * request's own-suffix attention by the merge rule of section "Online
+ * (cascade attention): the keys that many sequences have in common are
+ * scored once against every query of those sequences, and that partial result
+ * is then combined, per query, with the partial over the sequence's private
+ * keys by the merge rule of section "Online
  * softmax". Sequence b's keys are the prefix_len prefix tokens (token t in
  * page prefix_pages[t / page_size], slot t % page_size, of the same pools)
  * followed by its own kv_lens[b] tokens (block_table, as fa_forward_paged).
@@ -211,8 +212,8 @@ fa_status fa_cascade(const void* Q, const int32_t* qo_indptr,
  * num_splits == 0 picks ceil(seq_len / 256) clamped to [1, FA_MAX_SPLITS]:
  * chunks of at least 256 tokens, as many as allowed, so long and short
  * sequences alike spread over enough workgroups to keep HBM busy to the end
- * of the launch ("3.4 Attention Kernels", "In practice": kernels choose the
- * number of splits from the context length). Returns -1 for invalid input.
+ * of the launch ("3.4 Attention Kernels", "In practice": the split count
+ * follows from how long the context is). Returns -1 for invalid input.
  * Pure host function; the kernels evaluate the same rule on the device.
  */
 int fa_decode_num_splits(int seq_len, int num_splits);
@@ -231,8 +232,9 @@ size_t fa_decode_workspace_size(int B, int H, int d, int max_splits);
  *
  * Sequence b has seq_lens[b] cached tokens; token t lives in page
  * block_table[b * max_pages_per_seq + t / page_size] at slot t % page_size
- * ("3.4 Attention Kernels", "Paged and ragged layouts": the block table plus
- * the length of the last page, given here as the sequence length). Table
+ * ("3.4 Attention Kernels", "Paged and ragged layouts": pages found through
+ * a block table, the fill of the final page expressed here by the sequence
+ * length). Table
  * entries past the last used page are never read. The tokens are cut into
  * fa_decode_num_splits(seq_lens[b], num_splits) near-equal, page-aligned
  * chunks; each chunk's partial (o = acc / l, lse = m + ln l) is computed
@@ -307,8 +309,8 @@ fa_status fa_decode_paged_ex(const void* q, const void* K_pool,
  * "3.4 Attention Kernels", section "Kernel launch overhead and CUDA graphs":
  * a step made of short kernels is bound by the host's launch rate; recording
  * the launches once and replaying them as a graph removes that cost, provided
- * shapes and buffer addresses stay fixed, and callers copy each step's inputs
- * into the same buffers.
+ * shapes and buffer addresses stay fixed, so a caller refreshes the contents
+ * of the recorded buffers before every replay.
  *
  * fa_decode_graph_create validates exactly what fa_decode_paged_ex validates
  * (same arguments, same status codes, nothing recorded on error), then records

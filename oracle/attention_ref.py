@@ -470,6 +470,12 @@ def merge_partials(o_parts, lse_parts, num_parts=None):
 # split/merge invariants. These never stand in for the definition above.
 # ---------------------------------------------------------------------------
 
+def _rescale_factor(m_old: float, m_new: float) -> float:
+    """alpha = e^(m_old - m_new); a state that has seen nothing (m_old = -inf)
+    weighs 0."""
+    return 0.0 if m_old == -np.inf else float(np.exp(m_old - m_new))
+
+
 def online_softmax_row(scores, values, tile: int):
     """Softmax-weighted sum of `values` visited `tile` scores at a time.
 
@@ -490,21 +496,22 @@ def online_softmax_row(scores, values, tile: int):
     vals = _f64(values)
     if vals.ndim == 1:
         vals = vals[:, None]
-    m, l = -np.inf, 0.0
-    acc = np.zeros(vals.shape[1])
+    n = s.shape[0]
+    state = {"m": -np.inf, "l": 0.0, "acc": np.zeros(vals.shape[1])}
     trace = []
-    for i in range(0, len(s), tile):
-        blk, vblk = s[i:i + tile], vals[i:i + tile]
-        m_new = max(m, float(blk.max()))
-        factor = math.exp(m - m_new) if np.isfinite(m) else 0.0
-        l_resc, acc_resc = l * factor, acc * factor
-        e = np.exp(blk - m_new)
-        l = l_resc + e.sum()
-        acc = acc_resc + e @ vblk
-        trace.append(dict(m=m_new, factor=factor, l_rescaled=l_resc,
-                          acc_rescaled=acc_resc.copy(), l=l, acc=acc.copy()))
-        m = m_new
-    return acc / l, trace
+    for first in np.arange(0, n, tile):
+        block = slice(int(first), int(min(first + tile, n)))
+        m_next = max(state["m"], float(np.max(s[block])))
+        alpha = _rescale_factor(state["m"], m_next)
+        l_scaled = alpha * state["l"]
+        acc_scaled = alpha * state["acc"]
+        w = np.exp(s[block] - m_next)
+        state = {"m": m_next, "l": l_scaled + float(np.sum(w)),
+                 "acc": acc_scaled + w @ vals[block]}
+        trace.append(dict(m=m_next, factor=alpha, l_rescaled=l_scaled,
+                          acc_rescaled=acc_scaled.copy(), l=state["l"],
+                          acc=state["acc"].copy()))
+    return state["acc"] / state["l"], trace
 
 
 def split_kv_partials(q_row, k_rows, v_rows, scale: float, n_splits: int):
