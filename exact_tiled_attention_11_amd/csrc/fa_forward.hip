@@ -387,8 +387,7 @@ void fwd16_kernel(const FwdParams a) {
       if (k0 <= wave_last) {
         const uint16_t* kl = &smem[buf][0][0];
         const uint16_t* vl = &smem[buf][1][0];
-        // S^T = K Q^T: the two 32-key chains interleave and the K operands of
-        // step c+1 are read from LDS while step c multiplies.
+        // S^T = K Q^T: the two 32-key chains interleave.
         f32x16 s[2] = {f32x16{}, f32x16{}};
         {
           const uint16_t* row0 = kl + kr * D;
@@ -407,6 +406,16 @@ void fwd16_kernel(const FwdParams a) {
             s[1] = E::mma32(a1, qf[c], s[1]);
             a0 = n0v;
             a1 = n1v;
+          }
+          // Keep the K operand reads two steps ahead of the products that
+          // use them (left alone, the scheduler reuses one register pair and
+          // waits on every read). Groups: LDS reads (0x100), MFMA (0x008).
+          constexpr int kAhead = 2;
+          __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 0);
+#pragma unroll
+          for (int c = 0; c < QF; ++c) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            if (c + kAhead < QF) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
           }
         }
 
