@@ -113,7 +113,6 @@ struct TileLoader {
 
   // Rows past the last key re-read the last key (finite data whose scores
   // are masked to -inf, i.e. weight 0); only the ragged last tile needs it.
-  template <bool ASYNC = false>
   __device__ __forceinline__ void load(const uint16_t* kbase, const uint16_t* vbase, int64_t rs,
                                        int k0, int nk, uint16_t* kl, uint16_t* vl) const {
     const int64_t base = static_cast<int64_t>(k0) * rs;
@@ -122,13 +121,8 @@ struct TileLoader {
       int64_t shift = 0;
       if (k0 + kBC > nk)
         shift = static_cast<int64_t>(min(k0 + row[r], nk - 1) - k0 - row[r]) * rs;
-      if (ASYNC) {
-        load_lds16_async(kbase + base + off[r] + shift, kl + (slab0 + r) * 512);
-        load_lds16_async(vbase + base + off[r] + shift, vl + (slab0 + r) * 512);
-      } else {
-        load_lds16(kbase + base + off[r] + shift, kl + (slab0 + r) * 512);
-        load_lds16(vbase + base + off[r] + shift, vl + (slab0 + r) * 512);
-      }
+      load_lds16_async(kbase + base + off[r] + shift, kl + (slab0 + r) * 512);
+      load_lds16_async(vbase + base + off[r] + shift, vl + (slab0 + r) * 512);
     }
   }
 };
@@ -326,7 +320,7 @@ void fwd16_kernel(const FwdParams a) {
                    &smem[0][0][0], &smem[0][1][0]);
       if (n_steps > 1) ids_next = fetch_ids(tile_at(1));
     } else {
-      loader.template load<true>(kbase, vbase, kv_rs, tile_at(0) * kBC, Nk, &smem[0][0][0],
+      loader.load(kbase, vbase, kv_rs, tile_at(0) * kBC, Nk, &smem[0][0][0],
                                  &smem[0][1][0]);
     }
   }
@@ -380,7 +374,7 @@ void fwd16_kernel(const FwdParams a) {
                        &smem[nbuf][0][0], &smem[nbuf][1][0]);
           if (g + 2 < n_steps) ids_next = fetch_ids(tile_at(g + 2));
         } else {
-          loader.template load<true>(kbase, vbase, kv_rs, tile_at(g + ST - 1) * kBC, Nk,
+          loader.load(kbase, vbase, kv_rs, tile_at(g + ST - 1) * kBC, Nk,
                                      &smem[nbuf][0][0], &smem[nbuf][1][0]);
         }
       }
