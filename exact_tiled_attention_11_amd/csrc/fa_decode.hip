@@ -116,12 +116,15 @@ struct PageLoader {
                                         int64_t page_stride, int page_id, uint16_t* slot) const {
     const int pg = __builtin_amdgcn_readfirstlane(page_id);
     const int64_t pbase = static_cast<int64_t>(pg) * page_stride;
+    // Every cached byte is read exactly once: non-temporal loads keep the
+    // stream from displacing anything useful in L2 / MALL.
+    constexpr int kNonTemporal = 2;
 #pragma unroll
     for (int s = 0; s < Geo::SLABS; ++s)
-      load_lds16(kbase + pbase + koff[s], slot + s * 512);
+      load_lds16_policy<kNonTemporal>(kbase + pbase + koff[s], slot + s * 512);
 #pragma unroll
     for (int s = 0; s < Geo::SLABS; ++s)
-      load_lds16(vbase + pbase + voff[s], slot + Geo::PAGE_ELEMS + s * 512);
+      load_lds16_policy<kNonTemporal>(vbase + pbase + voff[s], slot + Geo::PAGE_ELEMS + s * 512);
   }
 };
 

@@ -50,10 +50,13 @@ __device__ __forceinline__ float sum_xor16(float v) {
 }
 
 // Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
-// lane i's 16 bytes land at lds + 16 * i; `lds` must be wave-uniform. The
-// explicit address-space casts keep the host compilation pass well-formed.
-__device__ __forceinline__ void load_lds16(const void* g, void* lds) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+// lane i's 16 bytes land at lds + 16 * i; `lds` must be wave-uniform. POLICY
+// is the instruction's cache-policy operand (2 = non-temporal). The explicit
+// address-space casts keep the host compilation pass well-formed.
+template <int POLICY>
+__device__ __forceinline__ void load_lds16_policy(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0,
+                                   POLICY);
 }
 
 // The same copy issued from inline assembly, for kernels that track these
