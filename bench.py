@@ -294,6 +294,18 @@ def bench_cascade(torch, fa, inputs, reps=10):
             "kv_bytes_decode": float(B * P + int(own.sum())) * kv_row}
 
 
+def stream_read_rate(torch, fa, nbytes=4 << 30, reps=20):
+    """Read bandwidth of the library's plain streaming-read kernel over a buffer
+    far larger than L2 and the last-level cache: what a memory-bound kernel
+    can reach here, beside the published peak."""
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    fa.stream_read(buf, sink)
+    ms = time_steps(torch, lambda: fa.stream_read(buf, sink), reps)
+    del buf
+    return dict(value=nbytes / (ms * 1e-3) / 1e9, unit="GB/s", bytes=nbytes, ms_mean=ms)
+
+
 def copy_calibration(torch, nbytes=1 << 30, reps=5):
     """A plain device copy of known size, for scaling HBM byte counters."""
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
@@ -417,6 +429,11 @@ def main():
         log("bench: cascade over a shared prefix")
         next_rows["cascade"] = bench_cascade(torch, fa, inputs)
 
+    read_rate = None
+    if "decode" in parts:
+        log("bench: plain streaming-read rate")
+        read_rate = stream_read_rate(torch, fa)
+
     pre_tflops = flops / (pre_ms.mean() * 1e-3) / 1e12 if "prefill" in parts else None
     dec_gbps = kv_bytes / (dec_ms.mean() * 1e-3) / 1e9 if "decode" in parts else None
     tr_pre, tr_dec = measured_traffic("prefill"), measured_traffic("decode")
@@ -458,6 +475,8 @@ def main():
             "frac": dec_gbps / HBM_PEAK_GBPS, "ms_mean": float(dec_ms.mean()),
             "ms_min": float(dec_ms.min()), "kv_bytes": kv_bytes,
             "timed": "decode kernel + merge kernel",
+            "stream_read": read_rate,
+            "frac_of_stream_read": dec_gbps / read_rate["value"] if read_rate else None,
             "traffic": tr_dec["hbm_bytes_per_launch"] if tr_dec else None,
             "traffic_detail": tr_dec},
         "cpu_baseline": cpu,

@@ -51,6 +51,7 @@ _SIGNATURES = {
     "fa_decode_graph_launch": (_I, [_P, _P]),
     "fa_decode_graph_destroy": (None, [_P]),
     "fa_merge_partials": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
+    "fa_stream_read": (_I, [_P, ctypes.c_size_t, _P, _P]),
     "fa_status_string": (ctypes.c_char_p, [_I]),
     "fa_version": (ctypes.c_char_p, []),
 }
@@ -351,3 +352,14 @@ def merge_partials(o_parts, lse_parts, num_parts=None, out_dtype=torch.float32, 
                                  R, S, d, _code(out_dtype), _stream(o_parts.device))
     _check(st, "fa_merge_partials")
     return out, lse
+
+
+def stream_read(buf: torch.Tensor, sink: torch.Tensor) -> None:
+    """Diagnostic: read every byte of the contiguous device tensor `buf` once
+    (the achievable-bandwidth yardstick for memory-bound kernels); `sink` is
+    a one-element int32 device tensor the kernel may write."""
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    _check(lib().fa_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(),
+                                _dev(sink, "sink", torch.int32), _stream(buf.device)),
+           "fa_stream_read")

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB_NAME = "libfa_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["fa_api.hip", "fa_forward.hip", "fa_decode.hip"]
+SOURCES = ["fa_api.hip", "fa_forward.hip", "fa_decode.hip", "fa_probe.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

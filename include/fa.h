@@ -371,6 +371,17 @@ fa_status fa_merge_partials(const float* o_parts, const float* lse_parts,
                             int R, int S, int d, fa_dtype out_dtype,
                             void* stream);
 
+/* Diagnostic, not part of the attention path: reads `bytes` of device memory
+ * at `buf` once, front to back, with 16-byte non-temporal loads spread over
+ * the whole chip, and writes nothing unless the data XOR to one fixed value
+ * (then one word to *sink). Its duration gives the read bandwidth a purely
+ * memory-bound kernel can reach on the device, the yardstick beside the
+ * published peak for the decode and merge kernels. buf must be 16-byte
+ * aligned and bytes a multiple of 16 (else FA_ERR_BAD_ARG); bytes == 0 does
+ * nothing; sink is a device pointer to one writable unsigned word. */
+fa_status fa_stream_read(const void* buf, size_t bytes, unsigned* sink,
+                         void* stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* fa_status_string(fa_status status);
 

@@ -264,3 +264,12 @@ def test_product_path_refuses_cpu_tensors():
     q = torch.zeros(1, 4, 1, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fa.forward(q, q, q)
+
+
+def test_stream_read_validation_before_any_hip_call():
+    lib = fa.lib()
+    assert lib.fa_stream_read(None, 0, None, None) == 0          # nothing to read
+    assert lib.fa_stream_read(None, 16, FAKE, None) == NULL
+    assert lib.fa_stream_read(FAKE, 16, None, None) == NULL
+    assert lib.fa_stream_read(ctypes.c_void_p(0x1008), 16, FAKE, None) == ARG
+    assert lib.fa_stream_read(FAKE, 24, FAKE, None) == ARG
