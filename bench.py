@@ -29,6 +29,7 @@ MFMA_BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 4096 dense bf16 FLOP/clk x 2.4 GHz
 HBM_PEAK_GBPS = 8000.0
 PREFILL = "causal_prefill_bf16_b4_h32_n8192"
 DECODE = "paged_decode_bf16_b64_h32_kv8"
+LONG = "long_causal_prefill_bf16_n65536"
 
 
 def log(*a):
@@ -210,6 +211,43 @@ def ragged_flops(q_lens, kv_lens, H, d, causal=True):
     return 4.0 * d * H * pairs
 
 
+def bench_long_prefill(torch, fa, inputs, reps=10):
+    """The long-context causal prefill (one sequence of 65536 tokens, 16 heads,
+    d = 128, bf16, Q scaled by 30), timed like the headline prefill."""
+    p = inputs.WORKLOADS[LONG].params
+    B, H, N, d = p["B"], p["H"], p["N"], p["d"]
+    q, k, v = inputs.prefill_inputs(B, H, p["Hkv"], N, N, d, torch.bfloat16, p["seed"],
+                                    q_scale=p["q_scales"][0])
+    q, k, v = q.cuda(), k.cuda(), v.cuda()
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+
+    def run():
+        fa.forward(q, k, v, causal=True, out=o, lse=lse)
+    for _ in range(2):
+        run()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for e0, e1 in evs:
+        e0.record()
+        run()
+        e1.record()
+    torch.cuda.synchronize()
+    import numpy as np
+    ms = np.array([a.elapsed_time(b) for a, b in evs])
+    fl = causal_flops(B, H, N, d)
+    tf = fl / (ms.mean() * 1e-3) / 1e12
+    tr = measured_traffic("long_prefill")
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+    return {"workload": LONG, "config": {k_: p[k_] for k_ in ("B", "H", "Hkv", "N", "d")} |
+            {"causal": True, "q_scale": p["q_scales"][0]},
+            "ms_mean": float(ms.mean()), "ms_min": float(ms.min()), "calls": reps,
+            "algorithmic_flop": fl, "value": tf, "unit": "TFLOP/s", "bound": "mfma",
+            "peak": MFMA_BF16_PEAK_TFLOPS, "frac": tf / MFMA_BF16_PEAK_TFLOPS,
+            "traffic": tr["hbm_bytes_per_launch"] if tr else None}
+
+
 def bench_forward_paged(torch, fa, inputs, reps=10):
     """Ragged queries over a paged cache: the causal-prefill shape with its K/V
     scattered over pages, and a continuous-batching step mixing prefill chunks
@@ -323,8 +361,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--parts", default="prefill,decode,variants,graph,paged,cascade",
-                    help="comma list: prefill, decode (the timed step), variants (windowed "
+    ap.add_argument("--parts", default="prefill,decode,long,variants,graph,paged,cascade",
+                    help="comma list: prefill, decode (the timed step), long (the 64K-token "
+                         "causal prefill), variants (windowed "
                          "and soft-capped decode), graph (graph-replayed decode step), paged "
                          "(ragged queries over a paged cache), cascade (shared-prefix decode)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -422,6 +461,11 @@ def main():
             log("bench: graph-replayed decode step")
             next_rows["decode_graph"] = bench_decode_graph(torch, fa, inputs, ddev, dp)
 
+    long_prefill = None
+    if "long" in parts:
+        log(f"bench: {LONG}")
+        long_prefill = bench_long_prefill(torch, fa, inputs)
+
     if "paged" in parts:
         log("bench: ragged queries over a paged cache")
         next_rows["forward_paged"] = bench_forward_paged(torch, fa, inputs)
@@ -479,6 +523,7 @@ def main():
             "frac_of_stream_read": dec_gbps / read_rate["value"] if read_rate else None,
             "traffic": tr_dec["hbm_bytes_per_launch"] if tr_dec else None,
             "traffic_detail": tr_dec},
+        "long_prefill": long_prefill,
         "cpu_baseline": cpu,
         "cpu_baseline_decode": cpu_dec,
         "next_rows": next_rows or None,
