@@ -49,6 +49,19 @@ __device__ __forceinline__ float sum_xor16(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// LDS reads at a 32-bit LDS byte address. Writing the address as a per-lane
+// base plus a constant lets the compiler fold the constant into the
+// instruction's offset field.
+template <typename T>
+__device__ __forceinline__ T lds_read16(uint32_t addr) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) T*>(static_cast<uintptr_t>(addr));
+}
+// Transposed read of a 4x4 block of 16-bit values (ds_read_b64_tr_b16).
+__device__ __forceinline__ i16x4 lds_read_tr8(uint32_t addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<__attribute__((address_space(3))) i16x4*>(static_cast<uintptr_t>(addr)));
+}
+
 // Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
 // lane i's 16 bytes land at lds + 16 * i; `lds` must be wave-uniform. POLICY
 // is the instruction's cache-policy operand (2 = non-temporal). The explicit
@@ -63,17 +76,30 @@ __device__ __forceinline__ void load_lds16_policy(const void* g, void* lds) {
 // loads themselves (explicit vmcnt waits and barriers). The compiler does not
 // see the LDS write, so it adds no conservative wait for all outstanding
 // vector-memory loads in front of later LDS reads, and the caller must order
-// every read of `lds` after the copy with s_waitcnt vmcnt + a barrier. M0
-// (the LDS destination register of the copy) is saved and restored around it.
-__device__ __forceinline__ void load_lds16_async(const void* g, const void* lds) {
-  const uint32_t a = __builtin_amdgcn_readfirstlane(
-      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds)));
+// every read of `lds` (an LDS byte address) after the copy with s_waitcnt
+// vmcnt + a barrier. M0 (the LDS destination register of the copy) is saved
+// and restored around it.
+__device__ __forceinline__ void load_lds16_async(const void* g, uint32_t lds) {
+  const uint32_t a = __builtin_amdgcn_readfirstlane(lds);
   uint32_t saved;
   __asm__ volatile(
       "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
       "global_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
       : "=&s"(saved)
       : "v"(g), "s"(a)
+      : "memory");
+}
+
+// The same copy from a wave-uniform base address plus a per-lane 32-bit byte
+// offset (the instruction's scalar-base form), to the LDS byte address
+// `lds` (wave-uniform). Stepping a tile then changes only scalar registers.
+__device__ __forceinline__ void load_lds16_sbase(const void* sbase, uint32_t voff, uint32_t lds) {
+  uint32_t saved;
+  __asm__ volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(sbase), "s"(lds)
       : "memory");
 }
 

@@ -21,9 +21,14 @@
 //     type, is directly the B operand of O^T += V^T P^T: no LDS round trip.
 //     The contraction over keys uses the keys in the order the score layout
 //     delivers them; V^T is fetched in that same key order.
+//   * Each wave runs a software pipeline over the key tiles: one step turns
+//     the scores of tile j into probabilities and adds P V(j), and in the
+//     same instruction stream computes the scores of tile j+1 on the matrix
+//     cores (see the comment at fwd16_kernel).
 //   * K and V tiles are copied from global memory straight into LDS (no
-//     register staging), one tile ahead of the one being computed. V stays
-//     row-major in LDS; the transposed operand comes from ds_read_b64_tr_b16.
+//     register staging, from a wave-uniform base address plus per-lane
+//     offsets), K two steps and V one step ahead. V stays row-major in LDS;
+//     the transposed operand comes from ds_read_b64_tr_b16.
 //   * Causal: a workgroup takes query blocks u and n-1-u of one head (the
 //     second with its key tiles in descending order), so all workgroups stream
 //     equally many tiles and those running together read the same tiles.
@@ -33,6 +38,8 @@
 // kept in fp32.
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
+
+#include <type_traits>
 
 namespace fa {
 namespace {
@@ -90,44 +97,52 @@ __device__ __forceinline__ int swz(int row) {
   }
 }
 
-// This wave's share of one K/V tile load, straight into LDS. Slab s covers
+// This wave's share of one K or V tile load, straight into LDS. Slab s covers
 // the LDS chunk slots 64s .. 64s+63 (1 KiB); lane l fills slot 64s + l with
 // the global 16-byte chunk (slot % CPR) ^ swz(row) of key row slot / CPR.
 template <int D, int NW>
 struct TileLoader {
   static constexpr int CPR = D / 8;
   static constexpr int SPW = kBC * CPR / 64 / NW;   // slabs per wave per tensor
-  int64_t off[SPW];   // element offset of this lane's chunk in key row k0 = 0
+  uint32_t voff[SPW];   // byte offset of this lane's chunk from key row k0
   int row[SPW];
-  int slab0;
+  int chunk[SPW];       // element offset of the chunk within its key row
+  uint32_t lds0;        // byte offset of this wave's first slab in a tile (wave-uniform)
 
   __device__ __forceinline__ TileLoader(int64_t rs, int wave, int lane) {
-    slab0 = wave * SPW;
+    const int slab0 = wave * SPW;
 #pragma unroll
     for (int r = 0; r < SPW; ++r) {
       const int slot = (slab0 + r) * 64 + lane;
       row[r] = slot / CPR;
-      off[r] = row[r] * rs + ((slot % CPR) ^ swz<D>(row[r])) * 8;
+      chunk[r] = ((slot % CPR) ^ swz<D>(row[r])) * 8;
+      voff[r] = static_cast<uint32_t>((row[r] * rs + chunk[r]) * 2);
     }
+    lds0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(slab0 * 1024));
   }
 
+  // Copies of this wave's slabs of the tile at key k0 into the tile at LDS
+  // byte address `lds`, from the wave-uniform row k0 plus per-lane offsets.
   // Rows past the last key re-read the last key (finite data whose scores
   // are masked to -inf, i.e. weight 0); only the ragged last tile needs it.
-  __device__ __forceinline__ void load(const uint16_t* kbase, const uint16_t* vbase, int64_t rs,
-                                       int k0, int nk, uint16_t* kl, uint16_t* vl) const {
-    const int64_t base = static_cast<int64_t>(k0) * rs;
+  __device__ __forceinline__ void load(const uint16_t* base, int64_t rs, int k0, int nk,
+                                       uint32_t lds) const {
+    const uint16_t* b0 = base + static_cast<int64_t>(k0) * rs;
+    if (__builtin_expect(k0 + kBC > nk, 0)) {
 #pragma unroll
-    for (int r = 0; r < SPW; ++r) {
-      int64_t shift = 0;
-      if (k0 + kBC > nk)
-        shift = static_cast<int64_t>(min(k0 + row[r], nk - 1) - k0 - row[r]) * rs;
-      load_lds16_async(kbase + base + off[r] + shift, kl + (slab0 + r) * 512);
-      load_lds16_async(vbase + base + off[r] + shift, vl + (slab0 + r) * 512);
+      for (int r = 0; r < SPW; ++r) {
+        uint32_t vo = static_cast<uint32_t>((min(row[r], nk - 1 - k0) * rs + chunk[r]) * 2);
+        __asm__("" : "+v"(vo));   // computed only on this (rare) path
+        load_lds16_sbase(b0, vo, lds + lds0 + r * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < SPW; ++r) load_lds16_sbase(b0, voff[r], lds + lds0 + r * 1024);
     }
   }
 };
 
-// The same share of a K/V tile when the keys live in 16-token pages: key
+// The same share of a K or V tile when the keys live in 16-token pages: key
 // k0 + row is slot row % 16 of page ids[row / 16] (a 64-key tile spans four
 // pages). Every slab lies inside one page.
 constexpr int kPageTokens = FA_PAGE_SIZE;
@@ -142,10 +157,11 @@ struct PagedTileLoader {
   static constexpr int RPS = 64 / CPR;                 // key rows per slab
   static constexpr int SPW = kBC * CPR / 64 / NW;
   static_assert(kPageTokens % RPS == 0, "a slab must not straddle pages");
-  int64_t roff[SPW];   // slot-in-page row offset + swizzled chunk offset
-  int coff[SPW];       // swizzled chunk offset alone
+  uint32_t voff[SPW];   // byte offset of this lane's chunk from the start of its page
+  int coff[SPW];        // swizzled chunk offset alone (elements)
   int row[SPW];
   int slab0;
+  uint32_t lds0;
 
   __device__ __forceinline__ PagedTileLoader(int64_t rs, int wave, int lane) {
     slab0 = wave * SPW;
@@ -154,28 +170,32 @@ struct PagedTileLoader {
       const int slot = (slab0 + r) * 64 + lane;
       row[r] = slot / CPR;
       coff[r] = ((slot % CPR) ^ swz<D>(row[r])) * 8;
-      roff[r] = (row[r] % kPageTokens) * rs + coff[r];
+      voff[r] = static_cast<uint32_t>(((row[r] % kPageTokens) * rs + coff[r]) * 2);
     }
+    lds0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(slab0 * 1024));
   }
 
-  // Rows past the last key re-read the last key, as in TileLoader.
-  __device__ __forceinline__ void load(const uint16_t* kbase, const uint16_t* vbase, int64_t rs,
-                                       int k0, int nk, int4 ids, uint16_t* kl,
-                                       uint16_t* vl) const {
+  // Copies of this wave's slabs of the tile at key k0, whose four page ids
+  // are `ids`, into the tile at LDS byte address `lds`. A slab lies in one
+  // page, so its base is wave-uniform. Rows past the last key re-read the
+  // last key, as in TileLoader (the ragged last tile, with per-lane pages).
+  __device__ __forceinline__ void load(const uint16_t* base, int64_t rs, int k0, int nk,
+                                       int4 ids, uint32_t lds) const {
     const int64_t pstride = rs * kPageTokens;
 #pragma unroll
     for (int r = 0; r < SPW; ++r) {
-      int64_t o;
+      const uint32_t dst = lds + lds0 + r * 1024;
       if (k0 + kBC <= nk) {
-        const int id = pick_id(ids, (slab0 + r) * RPS / kPageTokens);
-        o = static_cast<int64_t>(id) * pstride + roff[r];
+        const int id = __builtin_amdgcn_readfirstlane(
+            pick_id(ids, (slab0 + r) * RPS / kPageTokens));
+        load_lds16_sbase(base + static_cast<int64_t>(id) * pstride, voff[r], dst);
       } else {
         const int key = min(k0 + row[r], nk - 1);
         const int id = pick_id(ids, key / kPageTokens - k0 / kPageTokens);
-        o = static_cast<int64_t>(id) * pstride + (key % kPageTokens) * rs + coff[r];
+        load_lds16_async(base + static_cast<int64_t>(id) * pstride + (key % kPageTokens) * rs +
+                             coff[r],
+                         dst);
       }
-      load_lds16_async(kbase + o, kl + (slab0 + r) * 512);
-      load_lds16_async(vbase + o, vl + (slab0 + r) * 512);
     }
   }
 };
@@ -190,17 +210,35 @@ struct PagedTileLoader {
 // online softmax (up to rounding).
 __device__ __forceinline__ int tile_count(int last_key) { return last_key >= 0 ? last_key / kBC + 1 : 0; }
 
-constexpr int kFwdStages = 2;   // LDS slots: tiles are loaded one step ahead
+template <int P>
+using Parity = std::integral_constant<int, P>;
 
+// Software pipeline of one wave over the key tiles of a query block. Step j
+// turns the scores of tile j (computed at step j-1) into probabilities and
+// adds P V(j) to the output accumulator, and in the same instruction stream
+// computes the scores of tile j+1 on the matrix cores: the exponentials of
+// one tile run between the score products of the next, and the packing and
+// row sums between the P V products, in the same wave. (On CDNA4 vector work
+// hides behind matrix-core work of its own wave; spread over two waves of
+// one SIMD the two kinds of work mostly serialise.)
+//
+// LDS: K tiles in a 2-slot ring filled two steps ahead, V tiles in a 2-slot
+// ring filled one step ahead; counting the steps of a segment (one query
+// block) from 0, K of step x lives in K slot x & 1 and V of step x in V slot
+// x & 1. Step j reads K slot (j+1) & 1 and V slot j & 1 and issues the copies
+// of K(j+2) into K slot j & 1 and of V(j+1) into V slot (j+1) & 1, both freed
+// by the barrier that ends step j-1. The rings restart with every segment.
+// Every step is compiled once per parity of j, so that all LDS addresses are
+// per-lane constants plus immediate offsets.
 template <class E, typename OutT, int D, bool CAUSAL, int NW, bool PAGED>
 __global__ __launch_bounds__(NW * 64, 8 / NW)
 void fwd16_kernel(const FwdParams a) {
   constexpr int TILE = kBC * D;                 // elements per K or V tile
   constexpr int QF = D / 16;
+  constexpr int DB = D / 32;
   constexpr int BR = NW * kQPW;
-  constexpr int ST = kFwdStages;
-  constexpr int LPT = 2 * TileLoader<D, NW>::SPW;   // this wave's load instructions per tile
-  __shared__ __attribute__((aligned(16))) uint16_t smem[ST][2][TILE];   // [slot][K, V]
+  using V8 = typename E::vec8;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[4][TILE];   // K0 K1 V0 V1
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int bh, u;
@@ -273,12 +311,12 @@ void fwd16_kernel(const FwdParams a) {
     kbase += static_cast<int64_t>(b) * a.Nk * kv_rs;
     vbase += static_cast<int64_t>(b) * a.Nk * kv_rs;
   }
-  // Paged: the four page ids of a tile are fetched one step before its loads
-  // are issued and made wave-uniform only when used, after the step's barrier
-  // (so the wait for them never holds back K/V loads in flight). Ids past the
-  // sequence's last page are never used (rows past the last key re-read that
-  // key); an id outside the pool is replaced by page 0 and marks the sequence
-  // bad.
+  // Paged: page ids of a tile are fetched one step before they are needed and
+  // made wave-uniform only at the top of the step that uses them, when no
+  // K/V copy is in flight (so the wait for them never holds copies back).
+  // Ids past the sequence's last page are never used (rows past the last key
+  // re-read that key); an id outside the pool is replaced by page 0 and marks
+  // the sequence bad.
   const int32_t* table = PAGED ? a.block_table + static_cast<int64_t>(b) * a.max_pages : nullptr;
   const int last_page = Nk > 0 ? (Nk - 1) / kPageTokens : 0;
   bool bad_page = false;
@@ -300,34 +338,231 @@ void fwd16_kernel(const FwdParams a) {
     return make_int4(v[0], v[1], v[2], v[3]);
   };
 
-  // Per-lane LDS read geometry.
-  const int kr = lane & 31;                 // K operand row within a 32-key block
-  const int ksw = swz<D>(kr);
+  // Per-lane LDS read addresses (bytes, LDS address space) in the first K
+  // slot; other slots and key rows are immediate offsets from these.
+  // K operand of score step c, keys 0..31: row kr, chunk (2c + khi) ^ swz(kr);
+  // keys 32..63 are 32 rows further.
+  const uint32_t sbase = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&smem[0][0]));
+  const int kr = lane & 31;
   const int khi = lane >> 5;
+  uint32_t kaddr[QF];
+#pragma unroll
+  for (int c = 0; c < QF; ++c)
+    kaddr[c] = sbase + 2 * (kr * D + (((2 * c + khi) ^ swz<D>(kr)) * 8));
+  // Opaque to the optimiser, so every read uses the full per-lane address
+  // plus an immediate offset instead of re-adding a common base per step.
+#pragma unroll
+  for (int c = 0; c < QF; ++c) __asm__("" : "+v"(kaddr[c]));
+  // V^T operand of d block db (transposed 4x4 reads): rows vrow and vrow + 8
+  // of each 16-key group.
   const int blk = lane >> 4, r16 = lane & 15;
   const int vrow = 4 * (blk >> 1) + (r16 >> 2);          // 0..7
-  const int vsw0 = swz<D>(vrow), vsw1 = swz<D>(vrow + 8);
   const int vcl = 2 * (blk & 1) + ((r16 & 3) >> 1);      // chunk within a 32-wide d block
   const int vin = (r16 & 1) * 4;                          // element within the chunk
+  uint32_t vaddr0[DB], vaddr1[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    vaddr0[db] = sbase + 2 * (vrow * D + vin + (((4 * db + vcl) ^ swz<D>(vrow)) * 8));
+    vaddr1[db] = sbase + 2 * ((vrow + 8) * D + vin + (((4 * db + vcl) ^ swz<D>(vrow + 8)) * 8));
+    __asm__("" : "+v"(vaddr0[db]), "+v"(vaddr1[db]));
+  }
+  constexpr uint32_t kSlotBytes = TILE * 2;   // slot x of smem starts x * kSlotBytes in
 
   const TileLoader<D, NW> loader(kv_rs, wave, lane);
   const PagedTileLoader<D, NW> ploader(kv_rs, wave, lane);
-  int4 ids_next = make_int4(0, 0, 0, 0);   // fetched page ids of the tile of step g + 1
-  static_assert(ST == 2, "the page-id prefetch assumes tiles load one step ahead");
-  if (n_steps > 0) {
-    if constexpr (PAGED) {
-      ploader.load(kbase, vbase, kv_rs, tile_at(0) * kBC, Nk, use_ids(fetch_ids(tile_at(0))),
-                   &smem[0][0][0], &smem[0][1][0]);
-      if (n_steps > 1) ids_next = fetch_ids(tile_at(1));
-    } else {
-      loader.load(kbase, vbase, kv_rs, tile_at(0) * kBC, Nk, &smem[0][0][0],
-                                 &smem[0][1][0]);
+  // Paged: validated ids of the tile whose V is copied next (= the K tile of
+  // the previous step) and fetched ids of the K tile of the next step.
+  int4 ids_v = make_int4(0, 0, 0, 0), ids_next = make_int4(0, 0, 0, 0);
+  auto copy_k = [&](int g, int4 ids, uint32_t dst) {
+    if constexpr (PAGED)
+      ploader.load(kbase, kv_rs, tile_at(g) * kBC, Nk, ids, dst);
+    else
+      loader.load(kbase, kv_rs, tile_at(g) * kBC, Nk, dst);
+  };
+  auto copy_v = [&](int g, int4 ids, uint32_t dst) {
+    if constexpr (PAGED)
+      ploader.load(vbase, kv_rs, tile_at(g) * kBC, Nk, ids, dst);
+    else
+      loader.load(vbase, kv_rs, tile_at(g) * kBC, Nk, dst);
+  };
+  // First copies of a segment whose first step is g: K and V of step g into
+  // slot 0, K of step g + 1 into K slot 1 (when the segment has it).
+  auto segment_copies = [&](int g, int nt) {
+    if (nt <= 0) return;
+    int4 ids0 = make_int4(0, 0, 0, 0);
+    if constexpr (PAGED) ids0 = use_ids(fetch_ids(tile_at(g)));
+    copy_k(g, ids0, sbase);
+    copy_v(g, ids0, sbase + 2 * kSlotBytes);
+    if (nt > 1) {
+      if constexpr (PAGED) ids_v = use_ids(fetch_ids(tile_at(g + 1)));
+      copy_k(g + 1, ids_v, sbase + kSlotBytes);
+      if constexpr (PAGED)
+        if (nt > 2) ids_next = fetch_ids(tile_at(g + 2));
     }
-  }
+  };
 
-  int g = 0;                   // step counter over both blocks
-  int buf = 0;                 // slot of the tile of step g
-  int nbuf = ST - 1;           // slot that the tile of step g + ST - 1 loads into
+  // Scores of two key tiles; sc0 holds the tiles of the even steps of a
+  // segment, sc1 those of its odd steps.
+  f32x16 sc0[2], sc1[2];
+  f32x16 acc[DB];
+  float m_run, m2_run, l_run;   // this lane's query row
+  typename E::vec8 qf[QF];      // Q^T operand: lane l holds Q[row][16c + 8(l/32) .. +8]
+
+  // Scores S^T = K Q^T of the K tile in slot ks (no interleaving).
+  auto scores = [&](uint32_t ks, f32x16* s) {
+    const uint32_t o0 = ks * kSlotBytes, o1 = o0 + 32 * D * 2;
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+    V8 a0 = lds_read16<V8>(kaddr[0] + o0);
+    V8 a1 = lds_read16<V8>(kaddr[0] + o1);
+#pragma unroll
+    for (int c = 0; c < QF; ++c) {
+      V8 n0v = a0, n1v = a1;
+      if (c + 1 < QF) {
+        n0v = lds_read16<V8>(kaddr[c + 1] + o0);
+        n1v = lds_read16<V8>(kaddr[c + 1] + o1);
+      }
+      s[0] = E::mma32(a0, qf[c], s[0]);
+      s[1] = E::mma32(a1, qf[c], s[1]);
+      a0 = n0v;
+      a1 = n1v;
+    }
+  };
+
+  // P V for the V tile in slot vs: pb[2 kb + hh] holds the probabilities of
+  // keys 32kb + 16hh .. +16 in the order the score layout delivers them.
+  auto pv = [&](uint32_t vs, const V8* pb) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const uint32_t o = vs * kSlotBytes + (32 * kb + 16 * hh) * D * 2;
+          const i16x4 lo = lds_read_tr8(vaddr0[db] + o);
+          const i16x4 hi = lds_read_tr8(vaddr1[db] + o);
+          typedef short i16x8 __attribute__((ext_vector_type(8)));
+          const i16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          acc[db] = E::mma32(__builtin_bit_cast(V8, w), pb[2 * kb + hh], acc[db]);
+        }
+  };
+
+  // Probabilities of the scores s, in place: p = 2^(s*c - m2).
+  auto exps = [&](f32x16* s, float m2) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[kb][i] = exp2_fast(fmaf(s[kb][i], a.c, -m2));
+  };
+  // Matrix-core operands of the probabilities p (rounded to the input type).
+  auto pack = [&](const f32x16* p, V8* pb) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int o = 8 * hh;
+        pb[2 * kb + hh] = pack8<E>(p[kb][o + 0], p[kb][o + 1], p[kb][o + 2], p[kb][o + 3],
+                                   p[kb][o + 4], p[kb][o + 5], p[kb][o + 6], p[kb][o + 7]);
+      }
+  };
+  // Row sum of the probabilities p of this lane (its 32 keys of the tile).
+  auto rowsum = [&](const f32x16* p) {
+    float r0 = 0.f, r1 = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (i & 1) r1 += p[kb][i]; else r0 += p[kb][i];
+      }
+    return r0 + r1;
+  };
+
+  auto rescale = [&](float alpha) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+  };
+
+  // One pipelined step: scores of the next tile into `nx` (K slot ks),
+  // probabilities of `cur`, P V with the V tile in slot vs. The source order
+  // is the instruction order wanted: each score product is followed by two
+  // exponentials (with their argument FMAs) and the next K operand read, each
+  // P V product by the packing and row-sum work of its neighbours and the V
+  // operand reads of the next product.
+  auto fused = [&](uint32_t ks, uint32_t vs, f32x16* cur, f32x16* nx, float m2) {
+    constexpr int EPS = 32 / (2 * QF);   // exponentials per score product
+    const uint32_t o0 = ks * kSlotBytes, o1 = o0 + 32 * D * 2;
+    nx[0] = f32x16{};
+    nx[1] = f32x16{};
+    V8 a0 = lds_read16<V8>(kaddr[0] + o0);
+    V8 a1 = lds_read16<V8>(kaddr[0] + o1);
+#pragma unroll
+    for (int c = 0; c < QF; ++c) {
+      V8 n0v = a0, n1v = a1;
+      if (c + 1 < QF) n0v = lds_read16<V8>(kaddr[c + 1] + o0);
+      nx[0] = E::mma32(a0, qf[c], nx[0]);
+#pragma unroll
+      for (int e = 0; e < EPS; ++e) {
+        const int x = 2 * c * EPS + e;   // 0..31
+        cur[x >> 4][x & 15] = exp2_fast(fmaf(cur[x >> 4][x & 15], a.c, -m2));
+      }
+      if (c + 1 < QF) n1v = lds_read16<V8>(kaddr[c + 1] + o1);
+      nx[1] = E::mma32(a1, qf[c], nx[1]);
+#pragma unroll
+      for (int e = 0; e < EPS; ++e) {
+        const int x = (2 * c + 1) * EPS + e;
+        cur[x >> 4][x & 15] = exp2_fast(fmaf(cur[x >> 4][x & 15], a.c, -m2));
+      }
+      a0 = n0v;
+      a1 = n1v;
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int c = 0; c < 2 * QF; ++c) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, 2 * EPS, 0);
+      if (c + 2 < 2 * QF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // P V: product (kb, hh, db) uses pb[2kb + hh]; the operands of a pair
+    // (kb, hh) are packed just before its first product, and the row sum
+    // accumulates two probabilities per product.
+    float r0 = 0.f, r1 = 0.f;
+    V8 pb;
+    i16x4 lo = lds_read_tr8(vaddr0[0] + vs * kSlotBytes);
+    i16x4 hi = lds_read_tr8(vaddr1[0] + vs * kSlotBytes);
+#pragma unroll
+    for (int m = 0; m < 4 * DB; ++m) {
+      const int kb = m / (2 * DB), hh = (m / DB) & 1, db = m % DB;
+      if (db == 0) {
+        const int o = 8 * hh;
+        pb = pack8<E>(cur[kb][o + 0], cur[kb][o + 1], cur[kb][o + 2], cur[kb][o + 3],
+                      cur[kb][o + 4], cur[kb][o + 5], cur[kb][o + 6], cur[kb][o + 7]);
+      }
+      i16x4 nlo = lo, nhi = hi;
+      if (m + 1 < 4 * DB) {
+        const int kb1 = (m + 1) / (2 * DB), hh1 = ((m + 1) / DB) & 1, db1 = (m + 1) % DB;
+        const uint32_t o = vs * kSlotBytes + (32 * kb1 + 16 * hh1) * D * 2;
+        nlo = lds_read_tr8(vaddr0[db1] + o);
+        nhi = lds_read_tr8(vaddr1[db1] + o);
+      }
+      typedef short i16x8 __attribute__((ext_vector_type(8)));
+      const i16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      acc[db] = E::mma32(__builtin_bit_cast(V8, w), pb, acc[db]);
+      // Row sum: the 32 probabilities spread over the 4 DB products.
+#pragma unroll
+      for (int e = 0; e < 32 / (4 * DB); ++e) {
+        const int x = m * (32 / (4 * DB)) + e;
+        if (e & 1) r1 += cur[x >> 4][x & 15]; else r0 += cur[x >> 4][x & 15];
+      }
+      lo = nlo;
+      hi = nhi;
+    }
+    return r0 + r1;
+  };
+
+  int g = 0;   // step counter over both blocks
   for (int seg = 0; seg < nseg; ++seg) {
     const int qb = seg == 0 ? qb_first : qb_second;
     const int nt = seg == 0 ? n0 : n1;
@@ -339,9 +574,11 @@ void fwd16_kernel(const FwdParams a) {
     const int wave_last = qw0 >= nrows ? -1
                           : CAUSAL ? min(Nk - 1, (min(qw0 + kQPW, nrows) - 1) / G + off)
                                    : Nk - 1;
+    const int lim_row = CAUSAL ? min(Nk - 1, qrow + off) : Nk - 1;   // this lane's last key
 
-    // Q^T operand: lane l holds Q[row][16c + 8(l/32) .. +8].
-    typename E::vec8 qf[QF];
+    // The LDS rings restart with every segment (its step j uses the slots of
+    // parity j & 1): first copies, then this segment's query fragments.
+    segment_copies(g, nt);
     {
       const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
                            (q_row0 + qrow) * q_rs +
@@ -357,79 +594,57 @@ void fwd16_kernel(const FwdParams a) {
     // once, instead of at every score product of the loop.
 #pragma unroll
     for (int c = 0; c < QF; ++c) __asm__ volatile("" : "+v"(qf[c]));
-    if (seg == 0)
-      __asm__ volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __asm__ volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-    f32x16 acc[D / 32];
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
-    float m_run = kNegInf, m2_run = kNegInf, l_run = 0.f;   // this lane's query row
+    for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+    m_run = kNegInf;
+    m2_run = kNegInf;
+    l_run = 0.f;
 
-    for (int j = 0; j < nt; ++j, ++g) {
-      const int k0 = tile_at(g) * kBC;
-      const bool more = g + ST - 1 < n_steps;
-      if (more) {
+    // Scores of the segment's first tile, then a barrier: the first step
+    // refills the K slot they were read from.
+    bool cur_ok = nt > 0 && tile_at(g) * kBC <= wave_last;
+    if (cur_ok) scores(0, sc0);
+    __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+    // Step j of the segment (global step g).
+    auto step = [&](auto par, int j) {
+      constexpr int P = decltype(par)::value;   // parity of j
+      f32x16* cur = P ? sc1 : sc0;
+      f32x16* nx = P ? sc0 : sc1;
+      // Copies of K(j+2) and V(j+1) of this segment.
+      if (j + 2 < nt) {
+        int4 ids = make_int4(0, 0, 0, 0);
+        if constexpr (PAGED) ids = use_ids(ids_next);
+        copy_k(g + 2, ids, sbase + P * kSlotBytes);
+        copy_v(g + 1, ids_v, sbase + (3 - P) * kSlotBytes);
         if constexpr (PAGED) {
-          ploader.load(kbase, vbase, kv_rs, tile_at(g + 1) * kBC, Nk, use_ids(ids_next),
-                       &smem[nbuf][0][0], &smem[nbuf][1][0]);
-          if (g + 2 < n_steps) ids_next = fetch_ids(tile_at(g + 2));
-        } else {
-          loader.load(kbase, vbase, kv_rs, tile_at(g + ST - 1) * kBC, Nk,
-                                     &smem[nbuf][0][0], &smem[nbuf][1][0]);
+          ids_v = ids;
+          if (j + 3 < nt) ids_next = fetch_ids(tile_at(g + 3));
         }
+      } else if (j + 1 < nt) {
+        copy_v(g + 1, ids_v, sbase + (3 - P) * kSlotBytes);
       }
-      if (k0 <= wave_last) {
-        const uint16_t* kl = &smem[buf][0][0];
-        const uint16_t* vl = &smem[buf][1][0];
-        // S^T = K Q^T: the two 32-key chains interleave.
-        f32x16 s[2] = {f32x16{}, f32x16{}};
-        {
-          const uint16_t* row0 = kl + kr * D;
-          const uint16_t* row1 = row0 + 32 * D;
-          using V8 = typename E::vec8;
-          V8 a0 = *reinterpret_cast<const V8*>(row0 + ((khi ^ ksw) * 8));
-          V8 a1 = *reinterpret_cast<const V8*>(row1 + ((khi ^ ksw) * 8));
-#pragma unroll
-          for (int c = 0; c < QF; ++c) {
-            V8 n0v = a0, n1v = a1;
-            if (c + 1 < QF) {
-              n0v = *reinterpret_cast<const V8*>(row0 + (((2 * c + 2 + khi) ^ ksw) * 8));
-              n1v = *reinterpret_cast<const V8*>(row1 + (((2 * c + 2 + khi) ^ ksw) * 8));
-            }
-            s[0] = E::mma32(a0, qf[c], s[0]);
-            s[1] = E::mma32(a1, qf[c], s[1]);
-            a0 = n0v;
-            a1 = n1v;
-          }
-          // Keep the K operand reads two steps ahead of the products that
-          // use them (left alone, the scheduler reuses one register pair and
-          // waits on every read). Groups: LDS reads (0x100), MFMA (0x008).
-          constexpr int kAhead = 2;
-          __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 0);
-#pragma unroll
-          for (int c = 0; c < QF; ++c) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-            if (c + kAhead < QF) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-          }
-        }
-
+      const int k0 = tile_at(g) * kBC;
+      const bool nx_ok = j + 1 < nt && tile_at(g + 1) * kBC <= wave_last;
+      constexpr uint32_t kl = 1 - P;   // K slot of step j + 1
+      constexpr uint32_t vl = 2 + P;   // V slot of step j
+      if (cur_ok) {
         const bool need_mask = (k0 + kBC > Nk) || (CAUSAL && k0 + kBC - 1 > qw0 / G + off);
         if (need_mask) {
-          const int lim = CAUSAL ? min(Nk - 1, qrow + off) : Nk - 1;
+          const int rel = lim_row - k0 - 4 * khi;
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int key = k0 + 32 * kb + 8 * (i >> 2) + 4 * khi + (i & 3);
-              if (key > lim) s[kb][i] = kNegInf;
-            }
+            for (int i = 0; i < 16; ++i)
+              if (32 * kb + 8 * (i >> 2) + (i & 3) > rel) cur[kb][i] = kNegInf;
         }
-
         float mx = kNegInf;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, cur[kb][i]);
         mx = max_xor32(mx);
         // Exact running max: the largest probability of the row is exactly 1,
         // so it passes the rounding of P to the input type unchanged. A row
@@ -438,62 +653,31 @@ void fwd16_kernel(const FwdParams a) {
         const float m2_new = m_new * a.c;
         const float m2_use = (m_new == kNegInf) ? 0.f : m2_new;
         const float alpha = (m_new == m_run) ? 1.f : exp2_fast(m2_run - m2_new);
-        if (__any(alpha != 1.f)) {
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
-        }
-        float rs = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float p = exp2_fast(fmaf(s[kb][i], a.c, -m2_use));
-            s[kb][i] = p;
-            rs += p;
-          }
+        if (__any(alpha != 1.f)) rescale(alpha);
+        // The scores of the next tile are computed even when there is none
+        // (last step of the segment; they are then never used), so that this
+        // path is one straight instruction stream.
+        const float rs = fused(kl, vl, cur, nx, m2_use);
         l_run = fmaf(alpha, l_run, rs);
         m_run = m_new;
         m2_run = m2_new;
-
-        // O^T += V^T P^T, keys in the order the score layout holds them.
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const int o = 8 * hh;
-            const auto bop = pack8<E>(s[kb][o + 0], s[kb][o + 1], s[kb][o + 2], s[kb][o + 3],
-                                      s[kb][o + 4], s[kb][o + 5], s[kb][o + 6], s[kb][o + 7]);
-            const uint16_t* r0 = vl + (32 * kb + 16 * hh + vrow) * D + vin;
-            const uint16_t* r1 = r0 + 8 * D;
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-              const int ch = 4 * db + vcl;
-              const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                  (__attribute__((address_space(3))) i16x4*)(r0 + ((ch ^ vsw0) * 8)));
-              const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                  (__attribute__((address_space(3))) i16x4*)(r1 + ((ch ^ vsw1) * 8)));
-              typedef short i16x8 __attribute__((ext_vector_type(8)));
-              const i16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-              acc[db] = E::mma32(__builtin_bit_cast(typename E::vec8, w), bop, acc[db]);
-            }
-          }
-        }
+      } else if (nx_ok) {
+        scores(kl, nx);
       }
-      // The tile of step g+1 must be resident before the next step; younger
-      // tiles may still be in flight. Each wave waits for its own loads
-      // (issued from inline assembly, so the compiler does not track them),
-      // then all waves meet.
-      if (ST > 2 && more) {
-        __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"((ST > 2 ? ST - 2 : 0) * LPT) : "memory");
-      } else {
-        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      }
-      __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      buf = (buf + 1 == ST) ? 0 : buf + 1;
-      nbuf = (nbuf + 1 == ST) ? 0 : nbuf + 1;
+      cur_ok = nx_ok;
+      // The copies of this step must be resident before the next one, and
+      // every wave must be done with the slots they overwrite next. Each wave
+      // waits for its own copies (issued from inline assembly, so the
+      // compiler does not track them), then all waves meet.
+      __asm__ volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      ++g;
+    };
+    int j = 0;
+    for (; j + 1 < nt; j += 2) {
+      step(Parity<0>{}, j);
+      step(Parity<1>{}, j + 1);
     }
+    if (j < nt) step(Parity<0>{}, j);
 
     const float l_tot = sum_xor32(l_run);
     float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -507,7 +691,7 @@ void fwd16_kernel(const FwdParams a) {
         const int64_t pr = ((q_row0 + qrow) * a.H + h) * S + split;
         float* prow = a.part_o + pr * D;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
           for (int gg = 0; gg < 4; ++gg)
             store4(prow + 32 * db + 8 * gg + 4 * khi, acc[db][4 * gg] * inv,
@@ -519,7 +703,7 @@ void fwd16_kernel(const FwdParams a) {
       OutT* orow = static_cast<OutT*>(a.o) + (q_row0 + qrow) * q_rs +
                    static_cast<int64_t>(h) * D;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int gg = 0; gg < 4; ++gg)
           store4(orow + 32 * db + 8 * gg + 4 * khi, acc[db][4 * gg] * inv,
