@@ -117,6 +117,13 @@ struct BF16 {
   static __device__ __forceinline__ float to_f32(uint16_t u) {
     return __uint_as_float(static_cast<uint32_t>(u) << 16);
   }
+  // acc + v[2e] + v[2e+1] (one dot2 against (1, 1); the products are exact).
+  static __device__ __forceinline__ float sum2(vec8 v, int e, float acc) {
+    typedef __bf16 v2 __attribute__((ext_vector_type(2)));
+    const v2 p = {v[2 * e], v[2 * e + 1]};
+    const v2 one = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+    return __builtin_amdgcn_fdot2_f32_bf16(p, one, acc, false);
+  }
 };
 struct F16 {
   using scalar = _Float16;
@@ -129,6 +136,12 @@ struct F16 {
   }
   static __device__ __forceinline__ float to_f32(uint16_t u) {
     return static_cast<float>(__builtin_bit_cast(_Float16, u));
+  }
+  static __device__ __forceinline__ float sum2(vec8 v, int e, float acc) {
+    typedef _Float16 v2 __attribute__((ext_vector_type(2)));
+    const v2 p = {v[2 * e], v[2 * e + 1]};
+    const v2 one = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
+    return __builtin_amdgcn_fdot2(p, one, acc, false);
   }
 };
 

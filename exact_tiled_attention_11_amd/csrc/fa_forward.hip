@@ -49,6 +49,9 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kQPW = 32;              // query rows per wave
 constexpr int kBR = kWaves * kQPW;    // query rows per workgroup
 constexpr int kBC = 64;               // keys per tile
+// Largest growth (log2 units) of a row's max over the reference before the
+// 16-bit kernel rescales: probabilities stay below 2^kLazy.
+constexpr float kLazy = 8.f;
 
 struct FwdParams {
   const void* q;
@@ -405,7 +408,11 @@ void fwd16_kernel(const FwdParams a) {
   // segment, sc1 those of its odd steps.
   f32x16 sc0[2], sc1[2];
   f32x16 acc[DB];
-  float m_run, m2_run, l_run;   // this lane's query row
+  // This lane's query row: reference max m_run (raw score units) and m2_run =
+  // m_run * scale * log2(e); l_run = sum of 2^(s c - m2_run) over the keys
+  // so far; lt_run = the same sum over the values rounded to the input type,
+  // as the P V products use them.
+  float m_run, m2_run, l_run, lt_run;
   typename E::vec8 qf[QF];      // Q^T operand: lane l holds Q[row][16c + 8(l/32) .. +8]
 
   // Scores S^T = K Q^T of the K tile in slot ks (no interleaving).
@@ -526,9 +533,10 @@ void fwd16_kernel(const FwdParams a) {
     }
     __builtin_amdgcn_sched_barrier(0);
     // P V: product (kb, hh, db) uses pb[2kb + hh]; the operands of a pair
-    // (kb, hh) are packed just before its first product, and the row sum
-    // accumulates two probabilities per product.
-    float r0 = 0.f, r1 = 0.f;
+    // (kb, hh) are packed just before its first product. Two row sums
+    // accumulate between the products: of the probabilities (for the LSE)
+    // and of the rounded operands the products use (for normalising O).
+    float r0 = 0.f, r1 = 0.f, t0 = 0.f;
     V8 pb;
     i16x4 lo = lds_read_tr8(vaddr0[0] + vs * kSlotBytes);
     i16x4 hi = lds_read_tr8(vaddr1[0] + vs * kSlotBytes);
@@ -550,16 +558,19 @@ void fwd16_kernel(const FwdParams a) {
       typedef short i16x8 __attribute__((ext_vector_type(8)));
       const i16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       acc[db] = E::mma32(__builtin_bit_cast(V8, w), pb, acc[db]);
-      // Row sum: the 32 probabilities spread over the 4 DB products.
+      // Row sums: the 32 probabilities spread over the 4 DB products, the 8
+      // rounded operands of pb over its DB products.
 #pragma unroll
       for (int e = 0; e < 32 / (4 * DB); ++e) {
         const int x = m * (32 / (4 * DB)) + e;
         if (e & 1) r1 += cur[x >> 4][x & 15]; else r0 += cur[x >> 4][x & 15];
       }
+#pragma unroll
+      for (int e = db * 4 / DB; e < (db + 1) * 4 / DB; ++e) t0 = E::sum2(pb, e, t0);
       lo = nlo;
       hi = nhi;
     }
-    return r0 + r1;
+    return make_float2(r0 + r1, t0);
   };
 
   int g = 0;   // step counter over both blocks
@@ -601,6 +612,7 @@ void fwd16_kernel(const FwdParams a) {
     m_run = kNegInf;
     m2_run = kNegInf;
     l_run = 0.f;
+    lt_run = 0.f;
 
     // Scores of the segment's first tile, then a barrier: the first step
     // refills the K slot they were read from.
@@ -646,21 +658,34 @@ void fwd16_kernel(const FwdParams a) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) mx = fmaxf(mx, cur[kb][i]);
         mx = max_xor32(mx);
-        // Exact running max: the largest probability of the row is exactly 1,
-        // so it passes the rounding of P to the input type unchanged. A row
-        // whose keys in this tile are all masked keeps m = -inf, p = 0.
-        const float m_new = fmaxf(m_run, mx);
-        const float m2_new = m_new * a.c;
-        const float m2_use = (m_new == kNegInf) ? 0.f : m2_new;
-        const float alpha = (m_new == m_run) ? 1.f : exp2_fast(m2_run - m2_new);
-        if (__any(alpha != 1.f)) rescale(alpha);
+        // Thresholded running max: the reference m_run moves to the new row
+        // max (and the accumulators are rescaled by 2^(m2_old - m2_new)) only
+        // when some row of the wave exceeds it by more than kLazy in log2
+        // units; otherwise the probabilities of this tile are taken relative
+        // to the old reference, at most 2^kLazy. The result is the same
+        // function (the reference cancels in acc / l and enters LSE as
+        // m + ln l); O is normalised by the sum of the rounded probabilities
+        // the products used, so a row dominated by one key returns that key's
+        // value exactly. A row whose keys so far are all masked keeps
+        // m = -inf, p = 0.
+        const bool grow = (mx - m_run) * a.c > kLazy;
+        float m2_use = m2_run, alpha = 1.f;
+        if (__any(grow)) {
+          const float m_new = fmaxf(m_run, mx);
+          const float m2_new = m_new * a.c;
+          alpha = (m_new == m_run) ? 1.f : exp2_fast(m2_run - m2_new);
+          rescale(alpha);
+          m_run = m_new;
+          m2_run = m2_new;
+          m2_use = m2_new;
+        }
+        if (m_run == kNegInf) m2_use = 0.f;
         // The scores of the next tile are computed even when there is none
         // (last step of the segment; they are then never used), so that this
         // path is one straight instruction stream.
-        const float rs = fused(kl, vl, cur, nx, m2_use);
-        l_run = fmaf(alpha, l_run, rs);
-        m_run = m_new;
-        m2_run = m2_new;
+        const float2 rs = fused(kl, vl, cur, nx, m2_use);
+        l_run = fmaf(alpha, l_run, rs.x);
+        lt_run = fmaf(alpha, lt_run, rs.y);
       } else if (nx_ok) {
         scores(kl, nx);
       }
@@ -680,7 +705,8 @@ void fwd16_kernel(const FwdParams a) {
     if (j < nt) step(Parity<0>{}, j);
 
     const float l_tot = sum_xor32(l_run);
-    float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float lt_tot = sum_xor32(lt_run);
+    float inv = lt_tot > 0.f ? 1.f / lt_tot : 0.f;
     float lse_v = l_tot > 0.f ? (m2_run + log2f(l_tot)) * kLn2 : kNegInf;
     if (PAGED && (bad || bad_page)) {
       inv = __builtin_nanf("");
