@@ -163,17 +163,18 @@ struct PagedTileLoader {
   uint32_t voff[SPW];   // byte offset of this lane's chunk from the start of its page
   int coff[SPW];        // swizzled chunk offset alone (elements)
   int row[SPW];
-  int slab0;
+  int pidx[SPW];        // which of the tile's four pages slab r lies in (wave-uniform)
   uint32_t lds0;
 
   __device__ __forceinline__ PagedTileLoader(int64_t rs, int wave, int lane) {
-    slab0 = wave * SPW;
+    const int slab0 = wave * SPW;
 #pragma unroll
     for (int r = 0; r < SPW; ++r) {
       const int slot = (slab0 + r) * 64 + lane;
       row[r] = slot / CPR;
       coff[r] = ((slot % CPR) ^ swz<D>(row[r])) * 8;
       voff[r] = static_cast<uint32_t>(((row[r] % kPageTokens) * rs + coff[r]) * 2);
+      pidx[r] = __builtin_amdgcn_readfirstlane((slab0 + r) * RPS / kPageTokens);
     }
     lds0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(slab0 * 1024));
   }
@@ -185,20 +186,20 @@ struct PagedTileLoader {
   __device__ __forceinline__ void load(const uint16_t* base, int64_t rs, int k0, int nk,
                                        int4 ids, uint32_t lds) const {
     const int64_t pstride = rs * kPageTokens;
+    if (__builtin_expect(k0 + kBC > nk, 0)) {
 #pragma unroll
-    for (int r = 0; r < SPW; ++r) {
-      const uint32_t dst = lds + lds0 + r * 1024;
-      if (k0 + kBC <= nk) {
-        const int id = __builtin_amdgcn_readfirstlane(
-            pick_id(ids, (slab0 + r) * RPS / kPageTokens));
-        load_lds16_sbase(base + static_cast<int64_t>(id) * pstride, voff[r], dst);
-      } else {
+      for (int r = 0; r < SPW; ++r) {
         const int key = min(k0 + row[r], nk - 1);
         const int id = pick_id(ids, key / kPageTokens - k0 / kPageTokens);
         load_lds16_async(base + static_cast<int64_t>(id) * pstride + (key % kPageTokens) * rs +
                              coff[r],
-                         dst);
+                         lds + lds0 + r * 1024);
       }
+    } else {
+#pragma unroll
+      for (int r = 0; r < SPW; ++r)
+        load_lds16_sbase(base + static_cast<int64_t>(pick_id(ids, pidx[r])) * pstride, voff[r],
+                         lds + lds0 + r * 1024);
     }
   }
 };
