@@ -260,6 +260,27 @@ def test_forward_closed_forms(dt, d):
     assert np.abs(np64(l) - np.log(np.arange(1, 301))).max() <= 1e-4
 
 
+@pytest.mark.parametrize("growth", [-3.0, 0.5, 3.0, 7.9, 8.1, 20.0])
+@pytest.mark.parametrize("dt,causal", [("bf16", True), ("f16", False)])
+def test_forward_rising_scores(growth, dt, causal):
+    """Row maxima that climb steadily across the key tiles: every score gets a
+    ramp of `growth` log2 units per 64 keys on top of its random part. Slow
+    ramps keep an old reference max for many tiles (probabilities up to 2^8
+    on the 16-bit path), ramps near 8 sit at the rescale threshold, fast ramps
+    move the reference at every tile, a falling ramp puts the maximum first."""
+    B, H, N, d = 1, 2, 1024, 128
+    q, k, v = inputs.prefill_inputs(B, H, H, N, N, d, TD[dt], seed=21)
+    scale = 1 / math.sqrt(d)
+    beta = growth / (64 * scale * math.log2(math.e))
+    q = q.clone()
+    k = k.clone()
+    q[..., 0] = 1.0
+    k[..., 0] = (beta * torch.arange(N, dtype=torch.float32)).to(k.dtype)[None, :, None]
+    say(f"rising scores growth={growth} {dt} causal={causal}")
+    ro, rl = oracle.attention(q, k, v, scale, causal)
+    check_prefill(f"rising {growth} {dt}", q, k, v, causal, ro, rl)
+
+
 def test_forward_repeatable():
     q, k, v = inputs.prefill_inputs(2, 4, 4, 1000, 1000, 128, torch.bfloat16, seed=8)
     say("forward repeatability")
