@@ -14,9 +14,10 @@
 //   * one workgroup (4 waves) per (sequence, KV head, chunk); wave w takes
 //     pages w, w+4, ... of the chunk;
 //   * each wave streams its pages through a private ring of kStages page
-//     slots in LDS with direct-to-LDS loads (global_load_lds_dwordx4): three
-//     pages are in flight while one is processed, and no VGPR holds data in
-//     transit. The chunk's page ids are staged in LDS first;
+//     slots in LDS with direct-to-LDS loads (global_load_lds_dwordx4): the
+//     next page is in flight while one is processed (two workgroups per CU,
+//     so eight pages in flight per CU), and no VGPR holds data in transit.
+//     The chunk's page ids are staged in LDS first;
 //   * scores: S^T (16 tokens x 16 head slots) = K_page Q^T on one 16x16x32
 //     matrix-core op per 32 of d; lane l holds head slot l % 16 for tokens
 //     4(l/16) .. 4(l/16)+3, only the first G head slots are real;
