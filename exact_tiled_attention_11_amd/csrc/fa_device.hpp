@@ -103,6 +103,35 @@ __device__ __forceinline__ void load_lds16_sbase(const void* sbase, uint32_t vof
       : "memory");
 }
 
+// Buffer resource over `bytes` bytes from `base` for untyped loads (no
+// stride, no swizzle, 32-bit data format): a load whose offset lies at or
+// beyond `bytes` touches no memory and returns zeros. All fields are
+// wave-uniform.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(a)));
+  r[1] = __builtin_amdgcn_readfirstlane(static_cast<int>((a >> 32) & 0xFFFFu));
+  r[2] = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
+  r[3] = 0x00020000;
+  return r;
+}
+
+// Direct buffer -> LDS copy of 16 bytes per lane (buffer_load_dwordx4 with
+// lds): lane i reads the resource at byte offset voff (zeros when out of
+// range) and its 16 bytes land at LDS byte address lds + 16 * i (`lds`
+// wave-uniform). As for load_lds16_async, the caller orders later reads of
+// that LDS range with s_waitcnt vmcnt + a barrier; the compiler sets M0 (the
+// LDS destination register) from the operand.
+__device__ __forceinline__ void load_lds16_buf(i32x4 rsrc, uint32_t voff, uint32_t lds) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane(lds);
+  __asm__ volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                   :
+                   : "v"(voff), "s"(rsrc), "{m0}"(l)
+                   : "memory");
+}
+
 // Element types. Storage is handled as raw 16-bit words; arithmetic types
 // are the compiler's __bf16 / _Float16.
 struct BF16 {

@@ -132,16 +132,36 @@ struct TileLoader {
                                        uint32_t lds) const {
     const uint16_t* b0 = base + static_cast<int64_t>(k0) * rs;
     if (__builtin_expect(k0 + kBC > nk, 0)) {
-#pragma unroll
-      for (int r = 0; r < SPW; ++r) {
-        uint32_t vo = static_cast<uint32_t>((min(row[r], nk - 1 - k0) * rs + chunk[r]) * 2);
-        __asm__("" : "+v"(vo));   // computed only on this (rare) path
-        load_lds16_sbase(b0, vo, lds + lds0 + r * 1024);
-      }
+      load_clamped(b0, rs, nk - k0, lds);
     } else {
 #pragma unroll
       for (int r = 0; r < SPW; ++r) load_lds16_sbase(b0, voff[r], lds + lds0 + r * 1024);
     }
+  }
+  // The copies of a tile with only `left` (< kBC) keys from its first row b0
+  // to the end of the sequence.
+  __device__ __forceinline__ void load_clamped(const uint16_t* b0, int64_t rs, int left,
+                                               uint32_t lds) const {
+#pragma unroll
+    for (int r = 0; r < SPW; ++r) {
+      uint32_t vo = static_cast<uint32_t>((min(row[r], left - 1) * rs + chunk[r]) * 2);
+      __asm__("" : "+v"(vo));   // computed only on this (rare) path
+      load_lds16_sbase(b0, vo, lds + lds0 + r * 1024);
+    }
+  }
+
+  // Buffer resource of the tile whose first row is b0, with `left` keys from
+  // there to the end of the sequence: its rows past the last key (all rows
+  // when left <= 0) are out of range and copy as zeros without a memory
+  // access. (rows - 1) * rs + D <= Nk * rs elements, below 2^31 (the API's
+  // size limit), so the byte count fits 32 bits.
+  static __device__ __forceinline__ i32x4 rsrc(const uint16_t* b0, int rs, int left) {
+    const int rows = min(left, kBC);
+    return buffer_rsrc(b0, rows > 0 ? static_cast<uint32_t>((rows - 1) * rs + D) * 2u : 0u);
+  }
+  // Slab r of this wave's share of the tile of resource t.
+  __device__ __forceinline__ void load_buf(i32x4 t, int r, uint32_t lds) const {
+    load_lds16_buf(t, voff[r], lds + lds0 + r * 1024);
   }
 };
 
@@ -309,6 +329,7 @@ void fwd16_kernel(const FwdParams a) {
 
   const int64_t q_rs = static_cast<int64_t>(a.H) * D;
   const int64_t kv_rs = static_cast<int64_t>(a.Hkv) * D;
+  const int kv_rs32 = a.Hkv * D;
   const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + static_cast<int64_t>(hk) * D;
   const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + static_cast<int64_t>(hk) * D;
   if constexpr (!PAGED) {
@@ -437,54 +458,6 @@ void fwd16_kernel(const FwdParams a) {
     }
   };
 
-  // P V for the V tile in slot vs: pb[2 kb + hh] holds the probabilities of
-  // keys 32kb + 16hh .. +16 in the order the score layout delivers them.
-  auto pv = [&](uint32_t vs, const V8* pb) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const uint32_t o = vs * kSlotBytes + (32 * kb + 16 * hh) * D * 2;
-          const i16x4 lo = lds_read_tr8(vaddr0[db] + o);
-          const i16x4 hi = lds_read_tr8(vaddr1[db] + o);
-          typedef short i16x8 __attribute__((ext_vector_type(8)));
-          const i16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          acc[db] = E::mma32(__builtin_bit_cast(V8, w), pb[2 * kb + hh], acc[db]);
-        }
-  };
-
-  // Probabilities of the scores s, in place: p = 2^(s*c - m2).
-  auto exps = [&](f32x16* s, float m2) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[kb][i] = exp2_fast(fmaf(s[kb][i], a.c, -m2));
-  };
-  // Matrix-core operands of the probabilities p (rounded to the input type).
-  auto pack = [&](const f32x16* p, V8* pb) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int o = 8 * hh;
-        pb[2 * kb + hh] = pack8<E>(p[kb][o + 0], p[kb][o + 1], p[kb][o + 2], p[kb][o + 3],
-                                   p[kb][o + 4], p[kb][o + 5], p[kb][o + 6], p[kb][o + 7]);
-      }
-  };
-  // Row sum of the probabilities p of this lane (its 32 keys of the tile).
-  auto rowsum = [&](const f32x16* p) {
-    float r0 = 0.f, r1 = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        if (i & 1) r1 += p[kb][i]; else r0 += p[kb][i];
-      }
-    return r0 + r1;
-  };
-
   auto rescale = [&](float alpha) {
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -492,13 +465,35 @@ void fwd16_kernel(const FwdParams a) {
       for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
   };
 
+  // Copies of one step in the contiguous layout: this wave's slabs of the K
+  // tile of resource kt into the K slot at LDS byte address kl, and of the V
+  // tile vt into vl.
+  struct StepCopies {
+    i32x4 kt, vt;
+    uint32_t kl, vl;
+  };
+  // Issue copy x of the step's 2 * SPW copies (K slabs first).
+  auto issue_copy = [&](const StepCopies& cp, int x) {
+    constexpr int SPW = TileLoader<D, NW>::SPW;
+    if (x < SPW)
+      loader.load_buf(cp.kt, x, cp.kl);
+    else
+      loader.load_buf(cp.vt, x - SPW, cp.vl);
+  };
+
   // One pipelined step: scores of the next tile into `nx` (K slot ks),
   // probabilities of `cur`, P V with the V tile in slot vs. The source order
   // is the instruction order wanted: each score product is followed by two
   // exponentials (with their argument FMAs) and the next K operand read, each
   // P V product by the packing and row-sum work of its neighbours and the V
-  // operand reads of the next product.
-  auto fused = [&](uint32_t ks, uint32_t vs, f32x16* cur, f32x16* nx, float m2) {
+  // operand reads of the next product. With CP, the step's K/V copies `cp`
+  // are issued one by one between the first score products: issued together
+  // at the top of the step, the copies of all waves queue behind each other
+  // in the memory pipeline and every wave waits for its turn.
+  auto fused = [&](uint32_t ks, uint32_t vs, f32x16* cur, f32x16* nx, float m2, auto with_copies,
+                   const StepCopies& cp) {
+    constexpr bool CP = decltype(with_copies)::value;
+    constexpr int NCP = 2 * TileLoader<D, NW>::SPW;   // copies per step
     constexpr int EPS = 32 / (2 * QF);   // exponentials per score product
     const uint32_t o0 = ks * kSlotBytes, o1 = o0 + 32 * D * 2;
     nx[0] = f32x16{};
@@ -521,6 +516,11 @@ void fwd16_kernel(const FwdParams a) {
       for (int e = 0; e < EPS; ++e) {
         const int x = (2 * c + 1) * EPS + e;
         cur[x >> 4][x & 15] = exp2_fast(fmaf(cur[x >> 4][x & 15], a.c, -m2));
+      }
+      if constexpr (CP) {
+#pragma unroll
+        for (int x = 0; x < NCP; ++x)
+          if (c == x * (QF / 2) / NCP) issue_copy(cp, x);
       }
       a0 = n0v;
       a1 = n1v;
@@ -591,6 +591,14 @@ void fwd16_kernel(const FwdParams a) {
     // The LDS rings restart with every segment (its step j uses the slots of
     // parity j & 1): first copies, then this segment's query fragments.
     segment_copies(g, nt);
+    // Contiguous layout: key tile of the current step and the first row of
+    // its K and V; the tiles move up by one per step through the first block
+    // and down through the second.
+    const int dt = seg == 0 ? 1 : -1;
+    const int64_t dstep = static_cast<int64_t>(dt) * kBC * kv_rs;
+    int tcur = nt > 0 ? tile_at(g) : 0;
+    const uint16_t* kcur = kbase + static_cast<int64_t>(tcur) * kBC * kv_rs;
+    const uint16_t* vcur = vbase + static_cast<int64_t>(tcur) * kBC * kv_rs;
     {
       const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
                            (q_row0 + qrow) * q_rs +
@@ -626,18 +634,35 @@ void fwd16_kernel(const FwdParams a) {
       constexpr int P = decltype(par)::value;   // parity of j
       f32x16* cur = P ? sc1 : sc0;
       f32x16* nx = P ? sc0 : sc1;
-      // Copies of K(j+2) and V(j+1) of this segment.
-      if (j + 2 < nt) {
-        int4 ids = make_int4(0, 0, 0, 0);
-        if constexpr (PAGED) ids = use_ids(ids_next);
-        copy_k(g + 2, ids, sbase + P * kSlotBytes);
-        copy_v(g + 1, ids_v, sbase + (3 - P) * kSlotBytes);
-        if constexpr (PAGED) {
+      // Copies of K(j+2) and V(j+1) of this segment. Paged: here. Contiguous:
+      // between the score products of this step (or here, for a wave without
+      // rows in the current tile), from buffer resources that cover the
+      // tile's rows up to the sequence's last key. Rows past it, and the
+      // whole tile when the segment has no such step, copy as zeros: keys
+      // past the last one are masked, and a slot filled past the segment's
+      // end is not read before the next segment's first copies refill it.
+      StepCopies cp{};
+      if constexpr (PAGED) {
+        if (j + 2 < nt) {
+          const int4 ids = use_ids(ids_next);
+          copy_k(g + 2, ids, sbase + P * kSlotBytes);
+          copy_v(g + 1, ids_v, sbase + (3 - P) * kSlotBytes);
           ids_v = ids;
           if (j + 3 < nt) ids_next = fetch_ids(tile_at(g + 3));
+        } else if (j + 1 < nt) {
+          copy_v(g + 1, ids_v, sbase + (3 - P) * kSlotBytes);
         }
-      } else if (j + 1 < nt) {
-        copy_v(g + 1, ids_v, sbase + (3 - P) * kSlotBytes);
+      } else {
+        // keys from the first row of K(j+2) / V(j+1) to the end (0: no copy)
+        const int kleft = j + 2 < nt ? Nk - (tcur + 2 * dt) * kBC : 0;
+        const int vleft = j + 1 < nt ? Nk - (tcur + dt) * kBC : 0;
+        cp.kt = TileLoader<D, NW>::rsrc(kcur + 2 * dstep, kv_rs32, kleft);
+        cp.vt = TileLoader<D, NW>::rsrc(vcur + dstep, kv_rs32, vleft);
+        cp.kl = sbase + P * kSlotBytes;
+        cp.vl = sbase + (3 - P) * kSlotBytes;
+        tcur += dt;
+        kcur += dstep;
+        vcur += dstep;
       }
       const int k0 = tile_at(g) * kBC;
       const bool nx_ok = j + 1 < nt && tile_at(g + 1) * kBC <= wave_last;
@@ -684,11 +709,15 @@ void fwd16_kernel(const FwdParams a) {
         // The scores of the next tile are computed even when there is none
         // (last step of the segment; they are then never used), so that this
         // path is one straight instruction stream.
-        const float2 rs = fused(kl, vl, cur, nx, m2_use);
+        const float2 rs = fused(kl, vl, cur, nx, m2_use, std::integral_constant<bool, !PAGED>{}, cp);
         l_run = fmaf(alpha, l_run, rs.x);
         lt_run = fmaf(alpha, lt_run, rs.y);
-      } else if (nx_ok) {
-        scores(kl, nx);
+      } else {
+        if constexpr (!PAGED) {
+#pragma unroll
+          for (int x = 0; x < 2 * TileLoader<D, NW>::SPW; ++x) issue_copy(cp, x);
+        }
+        if (nx_ok) scores(kl, nx);
       }
       cur_ok = nx_ok;
       // The copies of this step must be resident before the next one, and
