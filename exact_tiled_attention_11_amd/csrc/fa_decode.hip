@@ -22,9 +22,12 @@
 //     matrix-core op per 32 of d; lane l holds head slot l % 16 for tokens
 //     4(l/16) .. 4(l/16)+3, only the first G head slots are real;
 //   * online softmax per head, two cross-row exchanges (l^16, l^32);
-//   * P V on the vector ALUs: probabilities and rescale factors reach the
-//     lanes that own 8 contiguous d of a few token rows through a per-wave
-//     LDS scratch;
+//   * P V on the matrix cores too, as O^T (16 d x 16 head slots) += V^T P^T
+//     on 16x16x16 ops: the probabilities leave the score op in exactly the
+//     layout of the P^T operand (lane l: head slot l % 16, tokens 4(l/16)
+//     .. +3), so they never leave the registers; the V^T operand comes from
+//     transposing LDS reads, and each head's rescale factor is in the lanes
+//     that hold its accumulators;
 //   * finally the 4 wave states are merged in LDS by the same rule and the
 //     chunk's (o, lse) is written: as the output when the sequence has one
 //     chunk, else as a partial for the merge kernel.
@@ -80,6 +83,12 @@ template <int D>
 __device__ __forceinline__ int kswz(int row) {
   return D == 128 ? row : (row >> 1) & 7;
 }
+// V rows likewise, so that the four token rows of one transposing read (32
+// bytes of each) fall into different banks.
+template <int D>
+__device__ __forceinline__ int vswz(int row) {
+  return D == 128 ? 2 * (row & 3) : 2 * ((row >> 1) & 1);
+}
 
 template <int D>
 struct DecGeom {
@@ -88,10 +97,8 @@ struct DecGeom {
   static constexpr int SLABS = PAGE_ELEMS * 2 / 1024; // 1 KiB wave-loads per tensor per page
   static constexpr int SLOT_ELEMS = 2 * PAGE_ELEMS;  // ring slot: K then V
   static constexpr int RING_ELEMS = kStages * SLOT_ELEMS;
-  static constexpr int LPR = D / 8;                  // lanes per token row in the P V layout
-  static constexpr int RPI = 64 / LPR;               // token rows per 16-byte load instruction
-  static constexpr int TPL = kPage / RPI;            // token rows per lane per page
-  static constexpr int NC = D / 32;                  // 16x16x32 steps over d
+  static constexpr int NC = D / 32;                  // 16x16x32 score steps over d
+  static constexpr int NB = D / 16;                  // 16-wide d blocks of P V
 };
 
 // One wave's direct-to-LDS loads of one page (K then V of one KV head) into
@@ -101,15 +108,15 @@ struct PageLoader {
   using Geo = DecGeom<D>;
   int koff[Geo::SLABS], voff[Geo::SLABS];   // element offsets from the page base
 
-  // Slab s of K fills ring slots 64s + lane (chunks permuted by kswz); V
-  // slots are not permuted.
+  // Slab s of K fills ring slots 64s + lane (chunks permuted by kswz), of V
+  // likewise (permuted by vswz).
   __device__ __forceinline__ PageLoader(int64_t row_stride, int lane) {
 #pragma unroll
     for (int s = 0; s < Geo::SLABS; ++s) {
       const int slot = s * 64 + lane;
       const int row = slot / Geo::CPR, ch = slot % Geo::CPR;
       koff[s] = static_cast<int>(row * row_stride) + ((ch ^ kswz<D>(row)) * 8);
-      voff[s] = static_cast<int>(row * row_stride) + ch * 8;
+      voff[s] = static_cast<int>(row * row_stride) + ((ch ^ vswz<D>(row)) * 8);
     }
   }
 
@@ -138,8 +145,6 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecParams a) 
 
   __shared__ __attribute__((aligned(16))) uint16_t ring[kDecWaves][Geo::RING_ELEMS];
   __shared__ int ids[kIdBatch];
-  __shared__ __attribute__((aligned(16))) float pbuf[kDecWaves][G][kPage];  // [head][token]
-  __shared__ float abuf[kDecWaves][G];
   __shared__ float wm[kDecWaves][G], wl[kDecWaves][G];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -177,16 +182,24 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecParams a) 
   }
 
   const PageLoader<D> loader(row_stride, lane);
-  // Per-lane read geometry: K operand (token hs, chunk 4c + grp) and the
-  // P V layout (d = 8e .. 8e+7 of token rows r*TPL .. r*TPL+TPL-1).
-  const int e = lane % Geo::LPR, r = lane / Geo::LPR;
+  // Per-lane read geometry. K operand of the scores: token hs, chunk
+  // 4c + grp. V^T operand of P V block nb (d = 16 nb .. +15): the 16 lanes
+  // of group grp read tokens 4 grp .. 4 grp + 3, lane hs supplying 4
+  // elements of token 4 grp + hs / 4 at d = 16 nb + 4 (hs % 4); the
+  // transposing read hands lane hs the 4 tokens of d = 16 nb + hs.
   uint16_t* my_ring = &ring[wave][0];
+  const uint32_t ring_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(my_ring));
+  const int vt = 4 * grp + (hs >> 2);
+  uint32_t vaddr[Geo::NB];
+#pragma unroll
+  for (int nb = 0; nb < Geo::NB; ++nb)
+    vaddr[nb] = ring_base + 2 * (Geo::PAGE_ELEMS + vt * D + 4 * (hs & 1) +
+                                 (((2 * nb + ((hs & 3) >> 1)) ^ vswz<D>(vt)) * 8));
 
-  float acc[G][8];
+  // O^T accumulators: lane l holds head slot hs, d = 16 nb + 4 grp + i.
+  f32x4 acc[Geo::NB];
 #pragma unroll
-  for (int n = 0; n < G; ++n)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[n][j] = 0.f;
+  for (int nb = 0; nb < Geo::NB; ++nb) acc[nb] = f32x4{};
   float m_run = kNegInf, m2_run = kNegInf, l_run = 0.f;   // head slot hs
   bool bad_page = false;
 
@@ -227,7 +240,6 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecParams a) 
         __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
       }
       const uint16_t* kl = my_ring + (k % kStages) * Geo::SLOT_ELEMS;
-      const uint16_t* vl = kl + Geo::PAGE_ELEMS;
       const int p = b0 + wave + k * kDecWaves;   // page index within the sequence
 
       // Scores for 16 tokens x 16 head slots.
@@ -264,58 +276,41 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecParams a) 
       l_run = fmaf(alpha, l_run, (pr[0] + pr[1]) + (pr[2] + pr[3]));
       m_run = m_new;
       m2_run = m2_new;
-      if (hs < G) {
-        *reinterpret_cast<float4*>(&pbuf[wave][hs][4 * grp]) = make_float4(pr[0], pr[1], pr[2], pr[3]);
-        if (grp == 0) abuf[wave][hs] = alpha;
+      // P^T operand (zero for the padding head slots) and the rescale of
+      // this lane's accumulators, whose head is its own.
+      const i16x4 pop = hs < G ? E::pack4(pr[0], pr[1], pr[2], pr[3]) : i16x4{};
+      if (__builtin_expect(__any(alpha != 1.f), 0)) {
+#pragma unroll
+        for (int nb = 0; nb < Geo::NB; ++nb) acc[nb] *= alpha;
       }
-      // The writes above and the reads below are this wave's own LDS traffic,
-      // completed in issue order.
-      __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-
-      // acc[n][:] = alpha_n acc[n][:] + sum_t p[n][t] V[t][8e..8e+7]
+      // V rows of tokens outside the visible range may hold anything (even
+      // NaN): their operand elements are zeroed on the pages that have them.
+      const uint32_t voff_slot = static_cast<uint32_t>((k % kStages) * Geo::SLOT_ELEMS * 2);
+      if (valid < kPage || lo > 0) {
+        int keep[4];
 #pragma unroll
-      for (int n = 0; n < G; ++n) {
-        const float al = abuf[wave][n];
+        for (int j = 0; j < 4; ++j) keep[j] = (4 * grp + j < valid && 4 * grp + j >= lo) ? -1 : 0;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[n][j] *= al;
-      }
+        for (int nb = 0; nb < Geo::NB; ++nb) {
+          i16x4 vop = lds_read_tr8(vaddr[nb] + voff_slot);
 #pragma unroll
-      for (int i = 0; i < Geo::TPL; ++i) {
-        const int t = r * Geo::TPL + i;
-        const uint4 raw = *reinterpret_cast<const uint4*>(vl + t * D + 8 * e);
-        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-        float vv[8];
-        const bool ok = t < valid && t >= lo;   // slots outside the visible range may hold anything
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          vv[2 * j] = ok ? E::to_f32(static_cast<uint16_t>(w[j] & 0xffffu)) : 0.f;
-          vv[2 * j + 1] = ok ? E::to_f32(static_cast<uint16_t>(w[j] >> 16)) : 0.f;
+          for (int j = 0; j < 4; ++j) vop[j] &= static_cast<short>(keep[j]);
+          acc[nb] = E::mma16k16(vop, pop, acc[nb]);
         }
+      } else {
 #pragma unroll
-        for (int n = 0; n < G; ++n) {
-          const float pn = pbuf[wave][n][t];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) acc[n][j] = fmaf(pn, vv[j], acc[n][j]);
-        }
+        for (int nb = 0; nb < Geo::NB; ++nb)
+          acc[nb] = E::mma16k16(lds_read_tr8(vaddr[nb] + voff_slot), pop, acc[nb]);
       }
+      // Every read of this slot is complete before the next iteration's
+      // copies may refill it.
       __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
   }
 
-  // Wave totals: l over the four token groups, acc over the token rows.
+  // Wave totals: l over the four token groups (acc already sums all tokens).
   float l_tot = sum_xor16(l_run);
   l_tot = sum_xor32(l_tot);
-#pragma unroll
-  for (int n = 0; n < G; ++n)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      float x = acc[n][j];
-      if (Geo::RPI == 8) x += __uint_as_float(__builtin_amdgcn_update_dpp(
-                              0u, __float_as_uint(x), 0x128, 0xf, 0xf, false));   // row_ror:8
-      x = sum_xor16(x);
-      x = sum_xor32(x);
-      acc[n][j] = x;
-    }
   // The ring is free once every wave has passed this barrier; the wave
   // states are merged in its memory.
   const bool bad = bad_len || __syncthreads_or(bad_page);
@@ -324,11 +319,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecParams a) 
     wm[wave][lane] = m2_run;
     wl[wave][lane] = l_tot;
   }
-  if (r == 0) {
+  if (hs < G) {
 #pragma unroll
-    for (int n = 0; n < G; ++n)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) wacc[(wave * G + n) * D + 8 * e + j] = acc[n][j];
+    for (int nb = 0; nb < Geo::NB; ++nb)
+      *reinterpret_cast<f32x4*>(&wacc[(wave * G + hs) * D + 16 * nb + 4 * grp]) = acc[nb];
   }
   __syncthreads();
 

@@ -8,6 +8,8 @@
 //   32x32x2 (f32):       lane l holds A[l%32][l/32] and B[l/32][l%32]; same C.
 //   16x16x32 (bf16/f16): lane l holds A[l%16][8*(l/16)+j], B[8*(l/16)+j][l%16];
 //                        result register i of lane l is C[4*(l/16)+i][l%16].
+//   16x16x16 (bf16/f16): lane l holds A[l%16][4*(l/16)+j], B[4*(l/16)+j][l%16]
+//                        (j = 0..3); same C as 16x16x32.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -143,6 +145,16 @@ struct BF16 {
   static __device__ __forceinline__ f32x4 mma16(vec8 a, vec8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
+  static __device__ __forceinline__ f32x4 mma16k16(i16x4 a, i16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+  }
+  // Round-to-nearest-even of 4 floats, as the raw 16-bit words of an operand.
+  static __device__ __forceinline__ i16x4 pack4(float a, float b, float c, float d) {
+    typedef __bf16 v4 __attribute__((ext_vector_type(4)));
+    const v4 r = {static_cast<__bf16>(a), static_cast<__bf16>(b), static_cast<__bf16>(c),
+                  static_cast<__bf16>(d)};
+    return __builtin_bit_cast(i16x4, r);
+  }
   static __device__ __forceinline__ float to_f32(uint16_t u) {
     return __uint_as_float(static_cast<uint32_t>(u) << 16);
   }
@@ -162,6 +174,17 @@ struct F16 {
   }
   static __device__ __forceinline__ f32x4 mma16(vec8 a, vec8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mma16k16(i16x4 a, i16x4 b, f32x4 c) {
+    typedef _Float16 v4 __attribute__((ext_vector_type(4)));
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(v4, a),
+                                                  __builtin_bit_cast(v4, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ i16x4 pack4(float a, float b, float c, float d) {
+    typedef _Float16 v4 __attribute__((ext_vector_type(4)));
+    const v4 r = {static_cast<_Float16>(a), static_cast<_Float16>(b), static_cast<_Float16>(c),
+                  static_cast<_Float16>(d)};
+    return __builtin_bit_cast(i16x4, r);
   }
   static __device__ __forceinline__ float to_f32(uint16_t u) {
     return static_cast<float>(__builtin_bit_cast(_Float16, u));
