@@ -83,11 +83,11 @@ template <int D>
 __device__ __forceinline__ int kswz(int row) {
   return D == 128 ? row : (row >> 1) & 7;
 }
-// V rows likewise, so that the four token rows of one transposing read (32
-// bytes of each) fall into different banks.
+// V rows likewise, so that the eight token rows one half-wave's transposing
+// read touches (32 bytes of each) fall into different banks.
 template <int D>
 __device__ __forceinline__ int vswz(int row) {
-  return D == 128 ? 2 * (row & 3) : 2 * ((row >> 1) & 1);
+  return D == 128 ? 2 * (row & 7) : 2 * ((row >> 1) & 3);
 }
 
 template <int D>
