@@ -263,6 +263,10 @@ void fwd16_kernel(const FwdParams a) {
   constexpr int BR = NW * kQPW;
   using V8 = typename E::vec8;
   __shared__ __attribute__((aligned(16))) uint16_t smem[4][TILE];   // K0 K1 V0 V1
+  // 16-bit outputs: each wave's 32 x D tile of O passes through LDS so that
+  // it is stored as whole rows.
+  constexpr bool kStageO = sizeof(OutT) == 2;
+  __shared__ __attribute__((aligned(16))) uint16_t ostage[kStageO ? NW * kQPW * D : 8];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int bh, u;
@@ -755,19 +759,52 @@ void fwd16_kernel(const FwdParams a) {
                    acc[db][4 * gg + 3] * inv);
         if (lane < 32) a.part_lse[pr] = lse_v;
       }
-    } else if (qrow < Nq) {
-      OutT* orow = static_cast<OutT*>(a.o) + (q_row0 + qrow) * q_rs +
-                   static_cast<int64_t>(h) * D;
+    } else {
+      if constexpr (kStageO) {
+        // The wave's O rows, rounded to the output type, into its LDS tile
+        // (16-byte chunks of a row permuted by an XOR with the row), then
+        // stored 16 contiguous bytes per lane: each store instruction
+        // writes four whole 2*D-byte rows.
+        constexpr int CPO = D / 8;   // 16-byte chunks per row
+        OutT* stile = reinterpret_cast<OutT*>(&ostage[0]) + wave * (kQPW * D);
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int gg = 0; gg < 4; ++gg)
-          store4(orow + 32 * db + 8 * gg + 4 * khi, acc[db][4 * gg] * inv,
-                 acc[db][4 * gg + 1] * inv, acc[db][4 * gg + 2] * inv, acc[db][4 * gg + 3] * inv);
+          for (int gg = 0; gg < 4; ++gg) {
+            const int ch = 4 * db + gg;
+            store4(stile + kr * D + ((ch ^ (kr % CPO)) * 8) + 4 * khi, acc[db][4 * gg] * inv,
+                   acc[db][4 * gg + 1] * inv, acc[db][4 * gg + 2] * inv,
+                   acc[db][4 * gg + 3] * inv);
+          }
+#pragma unroll
+        for (int j = 0; j < kQPW * CPO / 64; ++j) {
+          const int idx = j * 64 + lane;
+          const int row = idx / CPO, c = idx % CPO;
+          const int prow2 = qw0 + row;
+          const int qrow2 = prow2 / G;
+          const int h2 = hk * G + (prow2 - qrow2 * G);
+          const uint4 v = *reinterpret_cast<const uint4*>(stile + row * D + ((c ^ (row % CPO)) * 8));
+          typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+          if (qrow2 < Nq)
+            __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, v),
+                reinterpret_cast<u32x4_t*>(static_cast<OutT*>(a.o) + (q_row0 + qrow2) * q_rs +
+                                           static_cast<int64_t>(h2) * D + 8 * c));
+        }
+      } else if (qrow < Nq) {
+        OutT* orow = static_cast<OutT*>(a.o) + (q_row0 + qrow) * q_rs +
+                     static_cast<int64_t>(h) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int gg = 0; gg < 4; ++gg)
+            store4(orow + 32 * db + 8 * gg + 4 * khi, acc[db][4 * gg] * inv,
+                   acc[db][4 * gg + 1] * inv, acc[db][4 * gg + 2] * inv,
+                   acc[db][4 * gg + 3] * inv);
+      }
       // LSE layout: [B, H, Nq] dense; [total_q, H] for ragged queries.
       const int64_t li = PAGED ? (q_row0 + qrow) * a.H + h
                                : (static_cast<int64_t>(b) * a.H + h) * Nq + qrow;
-      if (lane < 32) a.lse[li] = lse_v;
+      if (lane < 32 && qrow < Nq) a.lse[li] = lse_v;
     }
   }
 }
