@@ -251,9 +251,12 @@ using Parity = std::integral_constant<int, P>;
 // block) from 0, K of step x lives in K slot x & 1 and V of step x in V slot
 // x & 1. Step j reads K slot (j+1) & 1 and V slot j & 1 and issues the copies
 // of K(j+2) into K slot j & 1 and of V(j+1) into V slot (j+1) & 1, both freed
-// by the barrier that ends step j-1. The rings restart with every segment.
+// by the barrier that ends step j-1 (dense layout: between its first score
+// products; paged: at its top). The rings restart with every segment.
 // Every step is compiled once per parity of j, so that all LDS addresses are
-// per-lane constants plus immediate offsets.
+// per-lane constants plus immediate offsets. With 16-bit outputs a further
+// per-wave LDS tile carries O on its way out, so that it is stored as whole
+// rows.
 template <class E, typename OutT, int D, bool CAUSAL, int NW, bool PAGED>
 __global__ __launch_bounds__(NW * 64, 8 / NW)
 void fwd16_kernel(const FwdParams a) {
