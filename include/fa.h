@@ -241,7 +241,9 @@ size_t fa_decode_workspace_size(int B, int H, int d, int max_splits);
  * independently and the partials are merged by the merge rule
  * ("Decode attention and Flash-Decoding"). All query heads that share a KV
  * head are processed together so each loaded K/V row serves all of them
- * (the GQA paragraph of the same section).
+ * (the GQA paragraph of the same section). Arithmetic as fa_forward: the
+ * scores and P V run on the matrix cores with fp32 accumulation, the
+ * probabilities rounded to the input type for the P V product.
  *
  * Layouts (row-major, contiguous):
  *   q            [B, H, d]                          dtype
