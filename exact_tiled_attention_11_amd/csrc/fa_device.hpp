@@ -33,9 +33,15 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 // Reductions across the two halves of a wave (lane l and lane l^32). Both
 // lanes of a pair combine the operands in the same order, so they end up
 // with bitwise identical values.
+// max of two floats that are never signalling NaNs (no quieting step).
+__device__ __forceinline__ float max_quiet(float a, float b) {
+  float r;
+  __asm__("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 __device__ __forceinline__ float max_xor32(float v) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max_quiet(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float sum_xor32(float v) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);

@@ -704,7 +704,7 @@ void fwd16_kernel(const FwdParams a) {
         const bool grow = (mx - m_run) * a.c > kLazy;
         float m2_use = m2_run, alpha = 1.f;
         if (__any(grow)) {
-          const float m_new = fmaxf(m_run, mx);
+          const float m_new = max_quiet(m_run, mx);
           const float m2_new = m_new * a.c;
           alpha = (m_new == m_run) ? 1.f : exp2_fast(m2_run - m2_new);
           rescale(alpha);
