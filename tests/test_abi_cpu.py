@@ -273,3 +273,15 @@ def test_stream_read_validation_before_any_hip_call():
     assert lib.fa_stream_read(FAKE, 16, None, None) == NULL
     assert lib.fa_stream_read(ctypes.c_void_p(0x1008), 16, FAKE, None) == ARG
     assert lib.fa_stream_read(FAKE, 24, FAKE, None) == ARG
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; asked for more it says so and exits before any GPU work."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
