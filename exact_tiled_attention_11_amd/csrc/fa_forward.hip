@@ -50,8 +50,11 @@ constexpr int kQPW = 32;              // query rows per wave
 constexpr int kBR = kWaves * kQPW;    // query rows per workgroup
 constexpr int kBC = 64;               // keys per tile
 // Largest growth (log2 units) of a row's max over the reference before the
-// 16-bit kernel rescales: probabilities stay below 2^kLazy.
-constexpr float kLazy = 8.f;
+// 16-bit kernel rescales: probabilities stay at or below 2^kLazy. bf16 and the
+// fp32 sums hold 2^32 with room to spare; fp16 (largest finite 65504) needs a
+// bound under 2^16.
+template <class E>
+constexpr float kLazy = std::is_same<E, BF16>::value ? 32.f : 8.f;
 
 struct FwdParams {
   const void* q;
@@ -701,7 +704,7 @@ void fwd16_kernel(const FwdParams a) {
         // the products used, so a row dominated by one key returns that key's
         // value exactly. A row whose keys so far are all masked keeps
         // m = -inf, p = 0.
-        const bool grow = (mx - m_run) * a.c > kLazy;
+        const bool grow = (mx - m_run) * a.c > kLazy<E>;
         float m2_use = m2_run, alpha = 1.f;
         if (__any(grow)) {
           const float m_new = max_quiet(m_run, mx);
