@@ -260,14 +260,15 @@ def test_forward_closed_forms(dt, d):
     assert np.abs(np64(l) - np.log(np.arange(1, 301))).max() <= 1e-4
 
 
-@pytest.mark.parametrize("growth", [-3.0, 0.5, 3.0, 7.9, 8.1, 20.0])
+@pytest.mark.parametrize("growth", [-3.0, 0.5, 3.0, 7.9, 8.1, 20.0, 31.9, 32.1])
 @pytest.mark.parametrize("dt,causal", [("bf16", True), ("f16", False)])
 def test_forward_rising_scores(growth, dt, causal):
     """Row maxima that climb steadily across the key tiles: every score gets a
     ramp of `growth` log2 units per 64 keys on top of its random part. Slow
-    ramps keep an old reference max for many tiles (probabilities up to 2^8
-    on the 16-bit path), ramps near 8 sit at the rescale threshold, fast ramps
-    move the reference at every tile, a falling ramp puts the maximum first."""
+    ramps keep an old reference max for many tiles (probabilities up to 2^32
+    with bf16 inputs, 2^8 with fp16), ramps near 32 (bf16) and 8 (fp16) sit at
+    the rescale thresholds, fast ramps move the reference at every tile, a
+    falling ramp puts the maximum first."""
     B, H, N, d = 1, 2, 1024, 128
     q, k, v = inputs.prefill_inputs(B, H, H, N, N, d, TD[dt], seed=21)
     scale = 1 / math.sqrt(d)
