@@ -106,7 +106,7 @@ typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
  * out_dtype == in_dtype or FA_F32; B, Nq, Nk >= 0; H, Hkv >= 1, H % Hkv == 0;
  * every tensor below 2^31 elements. B == 0 or Nq == 0 is a no-op. Nk == 0
  * writes O = 0 and LSE = -inf. Q, O, LSE (and K, V when Nk > 0) must be
- * non-NULL; scale must be finite.
+ * non-NULL; scale must be finite and positive (else FA_ERR_BAD_ARG).
  */
 fa_status fa_forward(const void* Q, const void* K, const void* V, void* O,
                      float* LSE, int B, int H, int Hkv, int Nq, int Nk, int d,
