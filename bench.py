@@ -26,6 +26,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 4096 dense bf16 FLOP/clk x 2.4 GHz
+FP32_PEAK_TFLOPS = 157.3         # published fp32 peak (matrix and vector)
 HBM_PEAK_GBPS = 8000.0
 PREFILL = "causal_prefill_bf16_b4_h32_n8192"
 DECODE = "paged_decode_bf16_b64_h32_kv8"
@@ -64,25 +65,35 @@ def causal_flops(B, H, N, d):
 
 
 def cpu_baseline_prefill(q, k, v, d, target_s):
-    """Time the float64 oracle on whole heads' worth of evenly spaced rows."""
+    """Time the float64 oracle as the parity tests call it: 256 evenly spaced
+    causal query rows per head, one block of rows (its default block size),
+    each row scored against every key of the sequence and the invisible ones
+    masked. `value` counts the algorithmic work of those rows (4 d per visible
+    query-key pair), the same measure as the GPU figure; `executed_tflops`
+    counts what the oracle actually multiplies (4 d per key of the whole row,
+    about twice as much for these rows)."""
     import numpy as np
     import oracle
     N = q.shape[1]
     rows = np.arange(N // 256 - 1, N, N // 256)            # 256 rows spread over the sequence
     per_head = sum(4.0 * d * (i + 1) for i in rows)
-    done, heads = 0.0, 0
+    per_head_exec = 4.0 * d * N * len(rows)
+    done, heads, b = 0.0, 0, 0
+    H = q.shape[2]
     t0 = time.perf_counter()
-    while time.perf_counter() - t0 < target_s and heads < q.shape[0] * q.shape[2]:
-        b, h = divmod(heads, q.shape[2])
-        oracle.attention(q[b:b + 1, :, h:h + 1], k[b:b + 1, :, h:h + 1], v[b:b + 1, :, h:h + 1],
-                         1 / math.sqrt(d), True, rows=rows, block_rows=16)
-        done += per_head
-        heads += 1
+    while time.perf_counter() - t0 < target_s and b < q.shape[0]:
+        # one batch entry, all heads: one job per head on the oracle's thread pool
+        oracle.attention(q[b:b + 1], k[b:b + 1], v[b:b + 1], 1 / math.sqrt(d), True, rows=rows)
+        done += per_head * H
+        heads += H
+        b += 1
     dt = time.perf_counter() - t0
     return dict(value=done / dt / 1e12, unit="TFLOP/s", cores=oracle.default_threads(),
-                kind="oracle",
-                sample=f"{heads} heads x 256 evenly spaced causal query rows of the "
-                       f"{PREFILL} workload, float64, {dt:.1f} s")
+                kind="oracle", executed_tflops=heads * per_head_exec / dt / 1e12,
+                sample=f"{heads} (batch, head) pairs x 256 evenly spaced causal query rows of "
+                       f"the {PREFILL} workload, float64, rows scored against all {N} keys "
+                       f"and masked (the oracle's own form); value counts visible pairs only; "
+                       f"{dt:.1f} s")
 
 
 def cpu_baseline_decode(pi, d, target_s):
@@ -122,7 +133,7 @@ def bench_decode_variants(torch, fa, inputs, pi, dev, lens, dp, steps):
     window, cap = 4096, 50.0
     vis = np.minimum(lens, window).astype(np.float64)
     kv = float(vis.sum()) * dp["Hkv"] * dp["d"] * 2 * 2
-    ws = torch.empty(fa.decode_workspace_size(dp["B"], dp["H"], dp["d"], fa.MAX_SPLITS),
+    ws = torch.empty(fa.decode_workspace_size(dp["B"], dp["H"], dp["Hkv"], dp["d"]),
                      dtype=torch.uint8, device="cuda")
     od = torch.empty_like(dev["q"])
     ld = torch.empty((dp["B"], dp["H"]), dtype=torch.float32, device="cuda")
@@ -138,6 +149,82 @@ def bench_decode_variants(torch, fa, inputs, pi, dev, lens, dp, steps):
             "frac_hbm": kv / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
 
 
+def bench_small_configs(torch, fa, inputs, reps=50):
+    """The two small forward workloads, timed like the others: one fp32 head of
+    256 x 256 (d = 64), and 12 heads of 2048 tokens (d = 64) causal and not, in
+    fp16 and fp32 with Q and 30 Q. TFLOP/s of algorithmic work (4 d per visible
+    query-key pair) against the published peak of the input type."""
+    out = {}
+    cases = [("single_head_f32_n256", 1, 1, 256, 64, "f32", False, 1.0)]
+    for dt in ("f16", "f32"):
+        for causal in (False, True):
+            for qs in (1.0, 30.0):
+                cases.append((f"mha12_d64_n2048_{dt}_{'causal' if causal else 'full'}_q{int(qs)}",
+                              1, 12, 2048, 64, dt, causal, qs))
+    for name, B, H, N, d, dt, causal, qs in cases:
+        wl = "single_head_f32_n256" if name.startswith("single") else "mha12_d64_n2048"
+        seed = inputs.WORKLOADS[wl].params["seed"]
+        q, k, v = inputs.prefill_inputs(B, H, H, N, N, d, inputs.TORCH_DTYPES[dt], seed,
+                                        q_scale=qs)
+        q, k, v = q.cuda(), k.cuda(), v.cuda()
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+
+        def run():
+            fa.forward(q, k, v, causal=causal, out=o, lse=lse)
+        for _ in range(3):
+            run()
+        ms = time_steps(torch, run, reps)
+        fl = causal_flops(B, H, N, d) if causal else 4.0 * d * N * N * B * H
+        peak = FP32_PEAK_TFLOPS if dt == "f32" else MFMA_BF16_PEAK_TFLOPS
+        tf = fl / (ms * 1e-3) / 1e12
+        out[name] = {"us_mean": ms * 1e3, "algorithmic_flop": fl, "value": tf,
+                     "unit": "TFLOP/s", "peak": peak, "frac": tf / peak, "calls": reps,
+                     "kernel": "fwd_kernel<fp32>" if dt == "f32" else "fwd16_kernel<f16, d=64>"}
+    return out
+
+
+def bench_decode_batch1(torch, fa, inputs, reps=20, copies=4):
+    """The pages' occupancy example: one sequence of 32768 cached tokens, 32
+    query heads over 8 KV heads, d = 128 (134 MB of K and V). Successive calls
+    read `copies` different caches in turn (537 MB in all, more than the 256 MB
+    last-level cache), so every call streams its KV from HBM."""
+    import numpy as np
+    H, Hkv, d, L = 32, 8, 128, 32768
+    lens = np.array([L], dtype=np.int64)
+    devs = []
+    for c in range(copies):
+        pi = inputs.paged_decode_inputs(1, H, Hkv, d, lens, seed=150 + c, pool_factor=1.0,
+                                        unreferenced="normal")
+        devs.append(dict(q=pi.q.cuda(), k=pi.k_pool.cuda(), v=pi.v_pool.cuda(),
+                         t=pi.block_table.cuda(), s=pi.seq_lens.cuda()))
+    kv = float(L) * Hkv * d * 2 * 2
+    o = torch.empty((1, H, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((1, H), dtype=torch.float32, device="cuda")
+    out = {"workload": "decode batch 1, 32768 tokens, h32/kv8, d128, bf16, 16-token pages",
+           "kv_bytes": kv, "caches_rotated": copies}
+    for splits in (0, 16, 32, 64):
+        ws = torch.empty(fa.decode_workspace_size(1, H, Hkv, d, splits), dtype=torch.uint8,
+                         device="cuda")
+        it = [0]
+
+        def run():
+            dv = devs[it[0] % copies]
+            it[0] += 1
+            fa.decode_paged(dv["q"], dv["k"], dv["v"], dv["t"], dv["s"], num_splits=splits,
+                            out=o, lse=lse, workspace=ws)
+        for _ in range(copies):
+            run()
+        ms = time_steps(torch, run, reps)
+        gbs = kv / (ms * 1e-3) / 1e9
+        key = "auto" if splits == 0 else f"splits_{splits}"
+        out[key] = {"splits": fa.decode_num_splits(L, 1, Hkv, splits), "us_mean": ms * 1e3,
+                    "value": gbs, "unit": "GB/s", "frac_hbm": gbs / HBM_PEAK_GBPS}
+    del devs
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_decode_graph(torch, fa, inputs, dev, dp, n=200):
     """Launch overhead: eager decode step (decode + merge launches) against one
     graph replay, on the paged-decode workload and on a one-sequence step."""
@@ -149,7 +236,7 @@ def bench_decode_graph(torch, fa, inputs, dev, dp, n=200):
                 t=spi.block_table.cuda(), s=spi.seq_lens.cuda())
     for name, d in (("b64_h32_kv8_paged", dev), ("b1_len1024", sdev)):
         B, H, hd = d["q"].shape
-        ws = torch.empty(fa.decode_workspace_size(B, H, hd, fa.MAX_SPLITS), dtype=torch.uint8,
+        ws = torch.empty(fa.decode_workspace_size(B, H, d["k"].shape[2], hd), dtype=torch.uint8,
                          device="cuda")
         o = torch.empty_like(d["q"])
         lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
@@ -310,7 +397,7 @@ def bench_cascade(torch, fa, inputs, reps=10):
         fa.cascade(q, ind, kp, vp, ppd, P, bt, kl, 1, causal=True, out=o, lse=lse, workspace=ws)
     full = torch.cat([prefix_pages.repeat(B, 1), ri.block_table], dim=1).cuda()
     full_lens = (ri.kv_lens + P).cuda()
-    dws = torch.empty(fa.decode_workspace_size(B, H, d, fa.MAX_SPLITS), dtype=torch.uint8,
+    dws = torch.empty(fa.decode_workspace_size(B, H, Hkv, d), dtype=torch.uint8,
                       device="cuda")
     o2 = torch.empty_like(o)
     l2 = torch.empty_like(lse)
@@ -361,11 +448,14 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--parts", default="prefill,decode,long,variants,graph,paged,cascade",
+    ap.add_argument("--parts",
+                    default="prefill,decode,long,small,batch1,variants,graph,paged,cascade",
                     help="comma list: prefill, decode (the timed step), long (the 64K-token "
-                         "causal prefill), variants (windowed "
-                         "and soft-capped decode), graph (graph-replayed decode step), paged "
-                         "(ragged queries over a paged cache), cascade (shared-prefix decode)")
+                         "causal prefill), small (the fp32 256-token head and the 12-head "
+                         "2048-token fp16/fp32 runs), batch1 (one 32K-token decode), variants "
+                         "(windowed and soft-capped decode), graph (graph-replayed decode "
+                         "step), paged (ragged queries over a paged cache), cascade "
+                         "(shared-prefix decode)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of each oracle baseline sample (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -417,7 +507,7 @@ def main():
         dt_, ds_ = pi.block_table.to(dev), pi.seq_lens.to(dev)
         od = torch.empty_like(dq)
         lsed = torch.empty((dp["B"], dp["H"]), dtype=torch.float32, device=dev)
-        ws = torch.empty(fa.decode_workspace_size(dp["B"], dp["H"], dp["d"], fa.MAX_SPLITS),
+        ws = torch.empty(fa.decode_workspace_size(dp["B"], dp["H"], dp["Hkv"], dp["d"]),
                          dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
@@ -465,6 +555,14 @@ def main():
     if "long" in parts:
         log(f"bench: {LONG}")
         long_prefill = bench_long_prefill(torch, fa, inputs)
+    small = None
+    if "small" in parts:
+        log("bench: single-head fp32 and 12-head d64 forward runs")
+        small = bench_small_configs(torch, fa, inputs)
+    batch1 = None
+    if "batch1" in parts:
+        log("bench: one-sequence 32K-token decode")
+        batch1 = bench_decode_batch1(torch, fa, inputs)
 
     if "paged" in parts:
         log("bench: ragged queries over a paged cache")
@@ -524,6 +622,8 @@ def main():
             "traffic": tr_dec["hbm_bytes_per_launch"] if tr_dec else None,
             "traffic_detail": tr_dec},
         "long_prefill": long_prefill,
+        "small_forward": small,
+        "decode_batch1_32k": batch1,
         "cpu_baseline": cpu,
         "cpu_baseline_decode": cpu_dec,
         "next_rows": next_rows or None,

@@ -18,11 +18,12 @@ import torch
 
 __all__ = [
     "FAError", "forward", "decode_paged", "merge_partials", "decode_num_splits",
-    "decode_workspace_size", "lib", "LIB_PATH", "MAX_SPLITS", "PAGE_SIZE", "version",
+    "decode_max_splits", "decode_workspace_size", "lib", "LIB_PATH", "MAX_SPLITS", "PAGE_SIZE",
+    "version",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa_mi355x.so")
-MAX_SPLITS = 16
+MAX_SPLITS = 64
 PAGE_SIZE = 16
 
 _DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
@@ -39,8 +40,9 @@ _SIGNATURES = {
     "fa_cascade_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "fa_cascade": (_I, [_P, _P, _P, _P, _P, _I, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I,
                         _I, _I, _F, _I, _I, _I, _P, ctypes.c_size_t, _P]),
-    "fa_decode_num_splits": (_I, [_I, _I]),
-    "fa_decode_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I]),
+    "fa_decode_max_splits": (_I, [_I, _I, _I]),
+    "fa_decode_num_splits": (_I, [_I, _I, _I, _I]),
+    "fa_decode_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
     "fa_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I,
                              _I, _I, _P, ctypes.c_size_t, _P]),
     "fa_decode_paged_ex": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F,
@@ -217,12 +219,19 @@ def cascade_workspace_size(total_q: int, H: int, d: int, num_splits: int) -> int
     return int(lib().fa_cascade_workspace_size(total_q, H, d, num_splits))
 
 
-def decode_num_splits(seq_len: int, num_splits: int = 0) -> int:
-    return lib().fa_decode_num_splits(int(seq_len), int(num_splits))
+def decode_max_splits(B: int, Hkv: int, num_splits: int = 0) -> int:
+    """Most key chunks a sequence of a B-sequence batch gets (partial slots per head)."""
+    return lib().fa_decode_max_splits(int(B), int(Hkv), int(num_splits))
 
 
-def decode_workspace_size(B: int, H: int, d: int, max_splits: int) -> int:
-    return int(lib().fa_decode_workspace_size(B, H, d, max_splits))
+def decode_num_splits(seq_len: int, B: int, Hkv: int, num_splits: int = 0) -> int:
+    """Key chunks of a sequence with seq_len visible tokens in a B-sequence batch."""
+    return lib().fa_decode_num_splits(int(seq_len), int(B), int(Hkv), int(num_splits))
+
+
+def decode_workspace_size(B: int, H: int, Hkv: int, d: int, num_splits: int = 0) -> int:
+    return int(lib().fa_decode_workspace_size(int(B), int(H), int(Hkv), int(d),
+                                              int(num_splits)))
 
 
 def _decode(entry, q, k_pool, v_pool, block_table, seq_lens, scale, num_splits, out_dtype, out,
@@ -239,8 +248,8 @@ def _decode(entry, q, k_pool, v_pool, block_table, seq_lens, scale, num_splits, 
     if lse is None:
         lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    S = num_splits if num_splits > 0 else MAX_SPLITS
-    need = decode_workspace_size(B, H, d, S) if B > 0 else 0
+    S = decode_max_splits(B, Hkv, num_splits) if B > 0 else 1
+    need = decode_workspace_size(B, H, Hkv, d, num_splits) if B > 0 else 0
     if workspace is None and S > 1 and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
@@ -295,8 +304,8 @@ class DecodeGraph:
                                                            device=q.device)
         self.lse = lse if lse is not None else torch.empty((B, H), dtype=torch.float32,
                                                            device=q.device)
-        S = num_splits if num_splits > 0 else MAX_SPLITS
-        need = decode_workspace_size(B, H, d, S) if B > 0 else 0
+        S = decode_max_splits(B, Hkv, num_splits) if B > 0 else 1
+        need = decode_workspace_size(B, H, Hkv, d, num_splits) if B > 0 else 0
         if workspace is None and S > 1 and need > 0:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
         self.workspace = workspace

@@ -15,6 +15,20 @@ namespace {
 
 constexpr int64_t kMaxElems = (int64_t{1} << 31) - 1;
 
+// HIP limits the threads of a launch along x (workgroups x workgroup size)
+// to 2^32 - 1.
+constexpr int64_t kMaxThreadsX = (int64_t{1} << 32) - 1;
+constexpr int64_t kFwd16Threads = 512;   // 8 waves
+constexpr int64_t kFwd32Threads = 256;   // 4 waves
+constexpr int64_t kMergeRowsPerBlock = 4, kMergeThreads = 256;
+bool grid_fits(int64_t workgroups, int64_t threads) {
+  return workgroups >= 0 && workgroups <= kMaxThreadsX / threads;
+}
+// Launch size of the merge kernel for R rows.
+bool merge_fits(int64_t rows) {
+  return grid_fits((rows + kMergeRowsPerBlock - 1) / kMergeRowsPerBlock, kMergeThreads);
+}
+
 bool valid_dtype(fa_dtype t) { return t == FA_F32 || t == FA_F16 || t == FA_BF16; }
 bool head_dim_ok(int d) { return d == 64 || d == 128; }
 bool scale_ok(float s) { return std::isfinite(s) && s > 0.f; }
@@ -32,6 +46,10 @@ int64_t forward16_grid(int64_t B, int64_t Hkv, int64_t group, int64_t max_q, boo
 
 // The kernels move data in 16-byte vectors.
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Query heads per KV head the decode kernels serve together (head slots of
+// their matrix-core tiles).
+constexpr int kMaxDecodeGroup = 16;
 
 }  // namespace
 
@@ -63,9 +81,11 @@ fa_status fa_forward(const void* Q, const void* K, const void* V, void* O, float
   if (out_dtype != in_dtype && out_dtype != FA_F32) return FA_ERR_UNSUPPORTED;
   const int64_t q_elems = int64_t{B} * Nq * H * d;
   const int64_t kv_elems = int64_t{B} * Nk * Hkv * d;
-  const int64_t grid = in_dtype == FA_F32 ? int64_t{B} * H * ((int64_t{Nq} + 127) / 128)
-                                          : forward16_grid(B, Hkv, H / Hkv, Nq, causal != 0);
-  if (q_elems > kMaxElems || kv_elems > kMaxElems || grid > kMaxElems) return FA_ERR_BAD_SHAPE;
+  const bool grid_ok =
+      in_dtype == FA_F32
+          ? grid_fits(int64_t{B} * H * ((int64_t{Nq} + 127) / 128), kFwd32Threads)
+          : grid_fits(forward16_grid(B, Hkv, H / Hkv, Nq, causal != 0), kFwd16Threads);
+  if (q_elems > kMaxElems || kv_elems > kMaxElems || !grid_ok) return FA_ERR_BAD_SHAPE;
   if (B == 0 || Nq == 0) return FA_OK;
   if (!Q || !O || !LSE || (Nk > 0 && (!K || !V))) return FA_ERR_NULL_PTR;
   if (!aligned16(Q) || !aligned16(O) || (Nk > 0 && (!aligned16(K) || !aligned16(V))))
@@ -92,7 +112,7 @@ fa_status fa_forward_paged(const void* Q, const int32_t* qo_indptr, const void* 
       int64_t{num_pages} * page_size * Hkv * d > kMaxElems ||
       int64_t{B} * max_pages_per_seq > kMaxElems ||
       int64_t{max_pages_per_seq} * page_size > kMaxElems ||
-      forward16_grid(B, Hkv, H / Hkv, max_q_len, causal != 0) > kMaxElems)
+      !grid_fits(forward16_grid(B, Hkv, H / Hkv, max_q_len, causal != 0), kFwd16Threads))
     return FA_ERR_BAD_SHAPE;
   if (B == 0 || total_q == 0 || max_q_len == 0) return FA_OK;
   if (!Q || !qo_indptr || !K_pool || !V_pool || !block_table || !kv_lens || !O || !LSE)
@@ -151,8 +171,9 @@ fa_status fa_cascade(const void* Q, const int32_t* qo_indptr, const void* K_pool
       int64_t{num_pages} * page_size * Hkv * d > kMaxElems ||
       int64_t{B} * max_pages_per_seq > kMaxElems ||
       int64_t{max_pages_per_seq} * page_size > kMaxElems ||
-      forward16_grid(B, Hkv, H / Hkv, max_q_len, causal != 0) > kMaxElems ||
-      forward16_grid(1, Hkv, H / Hkv, total_q, false) * S > kMaxElems)
+      !grid_fits(forward16_grid(B, Hkv, H / Hkv, max_q_len, causal != 0), kFwd16Threads) ||
+      !grid_fits(forward16_grid(1, Hkv, H / Hkv, total_q, false) * S, kFwd16Threads) ||
+      !merge_fits(int64_t{total_q} * H))
     return FA_ERR_BAD_SHAPE;
   if (total_q == 0) return FA_OK;
   if (!Q || !K_pool || !V_pool || !O || !LSE || (prefix_len > 0 && !prefix_pages) ||
@@ -208,14 +229,23 @@ fa_status fa_cascade(const void* Q, const int32_t* qo_indptr, const void* K_pool
   return from_hip(fa::launch_merge(m, st));
 }
 
-int fa_decode_num_splits(int seq_len, int num_splits) {
-  if (seq_len < 0 || num_splits < 0 || num_splits > FA_MAX_SPLITS) return -1;
-  return fa::decode_splits(seq_len, num_splits);
+int fa_decode_max_splits(int B, int Hkv, int num_splits) {
+  if (B < 0 || Hkv < 1 || num_splits < 0 || num_splits > FA_MAX_SPLITS) return -1;
+  return fa::decode_max_splits(B, Hkv, num_splits);
 }
 
-size_t fa_decode_workspace_size(int B, int H, int d, int max_splits) {
-  if (B < 0 || H < 1 || d < 1 || max_splits < 1 || max_splits > FA_MAX_SPLITS) return 0;
-  const size_t rows = static_cast<size_t>(B) * static_cast<size_t>(H) * max_splits;
+int fa_decode_num_splits(int seq_len, int B, int Hkv, int num_splits) {
+  if (seq_len < 0 || B < 1 || Hkv < 1 || num_splits < 0 || num_splits > FA_MAX_SPLITS)
+    return -1;
+  return fa::decode_splits(seq_len, fa::decode_max_splits(B, Hkv, num_splits), num_splits);
+}
+
+size_t fa_decode_workspace_size(int B, int H, int Hkv, int d, int num_splits) {
+  if (B < 0 || H < 1 || Hkv < 1 || H % Hkv != 0 || d < 1 || num_splits < 0 ||
+      num_splits > FA_MAX_SPLITS)
+    return 0;
+  const int S = fa::decode_max_splits(B, Hkv, num_splits);
+  const size_t rows = static_cast<size_t>(B) * static_cast<size_t>(H) * S;
   const size_t o_bytes = (rows * static_cast<size_t>(d) * sizeof(float) + 255) / 256 * 256;
   return o_bytes + rows * sizeof(float);
 }
@@ -224,6 +254,17 @@ size_t fa_decode_workspace_size(int B, int H, int d, int max_splits) {
 
 namespace {
 
+// The partial (o, lse) slots of a decode in `workspace`: o [B, H, S, d] fp32,
+// then lse [B, H, S] fp32 at the next 256-byte boundary.
+void set_partials(fa::DecodeArgs* a, void* workspace) {
+  const size_t rows = static_cast<size_t>(a->B) * a->H * a->max_splits;
+  a->part_o = static_cast<float*>(workspace);
+  a->part_lse = workspace ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                                     (rows * a->d * sizeof(float) + 255) / 256 *
+                                                         256)
+                          : nullptr;
+}
+
 // Validates a decode call and fills `a`; launches nothing. `*empty` is set
 // when the call is valid but has no work (B == 0).
 fa_status decode_prepare(const void* q, const void* K_pool, const void* V_pool,
@@ -231,7 +272,8 @@ fa_status decode_prepare(const void* q, const void* K_pool, const void* V_pool,
                          int B, int H, int Hkv, int d, int page_size, int max_pages_per_seq,
                          int num_pages, float scale, int num_splits, int window, float softcap,
                          fa_dtype dtype, fa_dtype out_dtype, void* workspace,
-                         size_t workspace_bytes, fa::DecodeArgs* out, bool* empty) {
+                         size_t workspace_bytes, fa::DecodeArgs* out, bool* empty,
+                         bool check_workspace = true) {
   *empty = false;
   if (B < 0 || H < 1 || Hkv < 1 || H % Hkv != 0 || max_pages_per_seq < 1 || num_pages < 1 ||
       page_size < 1)
@@ -241,13 +283,13 @@ fa_status decode_prepare(const void* q, const void* K_pool, const void* V_pool,
   if (!scale_ok(scale)) return FA_ERR_BAD_ARG;
   if (window < 0 || !std::isfinite(softcap) || softcap < 0.f) return FA_ERR_BAD_ARG;
   const int G = H / Hkv;
-  if (!head_dim_ok(d) || page_size != FA_PAGE_SIZE || dtype == FA_F32 ||
-      !(G == 1 || G == 2 || G == 4 || G == 8))
+  if (!head_dim_ok(d) || page_size != FA_PAGE_SIZE || dtype == FA_F32 || G > kMaxDecodeGroup)
     return FA_ERR_UNSUPPORTED;
   if (out_dtype != dtype && out_dtype != FA_F32) return FA_ERR_UNSUPPORTED;
   if (int64_t{num_pages} * page_size * Hkv * d > kMaxElems ||
       int64_t{B} * max_pages_per_seq > kMaxElems || int64_t{B} * H * d > kMaxElems ||
-      int64_t{max_pages_per_seq} * page_size > kMaxElems || B > 65535 || Hkv > 65535)
+      int64_t{max_pages_per_seq} * page_size > kMaxElems || B > 65535 || Hkv > 65535 ||
+      !merge_fits(int64_t{B} * H))
     return FA_ERR_BAD_SHAPE;
   if (B == 0) {
     *empty = true;
@@ -256,9 +298,10 @@ fa_status decode_prepare(const void* q, const void* K_pool, const void* V_pool,
   if (!q || !K_pool || !V_pool || !block_table || !seq_lens || !O || !LSE)
     return FA_ERR_NULL_PTR;
   if (!aligned16(q) || !aligned16(K_pool) || !aligned16(V_pool)) return FA_ERR_BAD_ARG;
-  const int S = num_splits > 0 ? num_splits : FA_MAX_SPLITS;
-  const size_t need = fa_decode_workspace_size(B, H, d, S);
-  if (S > 1 && (workspace == nullptr || workspace_bytes < need)) return FA_ERR_WORKSPACE;
+  const int S = fa::decode_max_splits(B, Hkv, num_splits);
+  const size_t need = fa_decode_workspace_size(B, H, Hkv, d, num_splits);
+  if (check_workspace && S > 1 && (workspace == nullptr || workspace_bytes < need))
+    return FA_ERR_WORKSPACE;
   fa::DecodeArgs a;
   a.q = q; a.k_pool = K_pool; a.v_pool = V_pool;
   a.block_table = block_table; a.seq_lens = seq_lens;
@@ -269,11 +312,7 @@ fa_status decode_prepare(const void* q, const void* K_pool, const void* V_pool,
   a.window = window; a.softcap = softcap;
   a.dtype = dtype; a.out_dtype = out_dtype;
   a.max_splits = S;
-  const size_t rows = static_cast<size_t>(B) * H * S;
-  a.part_o = static_cast<float*>(workspace);
-  a.part_lse = workspace ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                                    (rows * d * sizeof(float) + 255) / 256 * 256)
-                         : nullptr;
+  set_partials(&a, workspace);
   *out = a;
   return FA_OK;
 }
@@ -385,7 +424,7 @@ fa_status fa_merge_partials(const float* o_parts, const float* lse_parts, const 
                             void* stream) {
   if (R < 0 || S < 1 || S > 1024 || d < 1 || d > 1024) return FA_ERR_BAD_SHAPE;
   if (!valid_dtype(out_dtype)) return FA_ERR_BAD_ARG;
-  if (int64_t{R} * S * d > kMaxElems) return FA_ERR_BAD_SHAPE;
+  if (int64_t{R} * S * d > kMaxElems || !merge_fits(R)) return FA_ERR_BAD_SHAPE;
   if (R == 0) return FA_OK;
   if (!o_parts || !lse_parts || !O || !LSE) return FA_ERR_NULL_PTR;
   fa::MergeArgs a{o_parts, lse_parts, num_parts, O, LSE, R, S, d, out_dtype};

@@ -61,6 +61,7 @@ struct DecParams {
   float* part_o;
   float* part_lse;
   int B, H, Hkv, max_pages, num_pages, num_splits, max_splits;
+  int group;             // H / Hkv: query heads sharing one KV head (<= head slots)
   float c;   // scale * log2(e)
   int window;            // > 0: only the newest `window` keys are visible
   int softcap_on;        // 1: scores are soft-capped
@@ -136,23 +137,26 @@ struct PageLoader {
   }
 };
 
-template <class E, typename OutT, int D, int G>
+// GP: head slots in use, a power of two >= the group size a.group (the
+// remaining slots carry zero queries and are never stored).
+template <class E, typename OutT, int D, int GP>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecParams a) {
   using Geo = DecGeom<D>;
-  static_assert(G >= 1 && G <= 16, "head group must fit the 16 head slots");
-  static_assert(kDecWaves * G * D * 4 <= kDecWaves * Geo::RING_ELEMS * 2,
+  static_assert(GP >= 1 && GP <= 16, "head group must fit the 16 head slots");
+  static_assert(kDecWaves * GP * D * 4 <= kDecWaves * Geo::RING_ELEMS * 2,
                 "wave states must fit in the ring for the final merge");
 
   __shared__ __attribute__((aligned(16))) uint16_t ring[kDecWaves][Geo::RING_ELEMS];
   __shared__ int ids[kIdBatch];
-  __shared__ float wm[kDecWaves][G], wl[kDecWaves][G];
+  __shared__ float wm[kDecWaves][GP], wl[kDecWaves][GP];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+  const int G = a.group;
   const int len = a.seq_lens[b];
   const bool bad_len = len < 0 || len > a.max_pages * kPage;
   const int kv_start = bad_len ? 0 : first_visible(len, a.window);
-  const int nsplit = decode_splits(bad_len ? 0 : len - kv_start, a.num_splits);
+  const int nsplit = decode_splits(bad_len ? 0 : len - kv_start, a.max_splits, a.num_splits);
   if (split >= nsplit) return;                 // whole workgroup: uniform
   const int npages = bad_len ? 0 : (len + kPage - 1) / kPage;
   const int p0 = kv_start / kPage;             // first page holding a visible key
@@ -315,14 +319,14 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecParams a) 
   // states are merged in its memory.
   const bool bad = bad_len || __syncthreads_or(bad_page);
   float* wacc = reinterpret_cast<float*>(&ring[0][0]);   // [wave][G][D]
-  if (lane < G) {
+  if (lane < GP) {
     wm[wave][lane] = m2_run;
     wl[wave][lane] = l_tot;
   }
-  if (hs < G) {
+  if (hs < GP) {
 #pragma unroll
     for (int nb = 0; nb < Geo::NB; ++nb)
-      *reinterpret_cast<f32x4*>(&wacc[(wave * G + hs) * D + 16 * nb + 4 * grp]) = acc[nb];
+      *reinterpret_cast<f32x4*>(&wacc[(wave * GP + hs) * D + 16 * nb + 4 * grp]) = acc[nb];
   }
   __syncthreads();
 
@@ -338,7 +342,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecParams a) 
       for (int w = 0; w < kDecWaves; ++w) {
         const float wt = exp2_fast(wm[w][n] - M);
         lsum = fmaf(wt, wl[w][n], lsum);
-        osum = fmaf(wt, wacc[(w * G + n) * D + dd], osum);
+        osum = fmaf(wt, wacc[(w * GP + n) * D + dd], osum);
       }
     }
     float o = lsum > 0.f ? osum / lsum : 0.f;
@@ -370,7 +374,7 @@ struct MergeParams {
   float* lse;
   int R, S, d;
   int heads;                  // decode mode: rows per sequence
-  int fixed_splits;           // decode mode: num_splits argument
+  int fixed_splits;           // decode mode: num_splits argument (0: the rule, capped at S)
   int max_len;                // decode mode: max_pages * page_size
   int window;                 // decode mode: visible-key window (0 = all)
   const float* o_extra;       // optional part S of every row: [R, d] ...
@@ -389,7 +393,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams a) {
   if (DECODE) {
     const int len = a.seq_lens[r / a.heads];
     const bool bad = len < 0 || len > a.max_len;
-    n = decode_splits(bad ? 0 : len - first_visible(len, a.window), a.fixed_splits);
+    n = decode_splits(bad ? 0 : len - first_visible(len, a.window), a.S, a.fixed_splits);
     if (n <= 1) return;   // written directly by the decode kernel
   } else {
     n = a.num_parts ? a.num_parts[r] : a.S;
@@ -440,9 +444,8 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams a) {
   for (int x = lane; x < a.d; x += 64) {
     float acc = 0.f;
     if (DECODE) {
-#pragma unroll
-      for (int c = 0; c < FA_MAX_SPLITS; ++c)
-        if (c < n) acc = fmaf(wsh[wave][c], o_r[c * a.d + x], acc);
+#pragma unroll 8
+      for (int c = 0; c < n; ++c) acc = fmaf(wsh[wave][c], o_r[c * a.d + x], acc);
     } else {
       for (int c = 0; c < n; ++c) acc = fmaf(wsh[wave][c], o_r[c * a.d + x], acc);
       if (a.o_extra) acc = fmaf(we, a.o_extra[r * a.d + x], acc);
@@ -472,13 +475,18 @@ hipError_t merge_dispatch(const MergeParams& p, fa_dtype out, hipStream_t s) {
 
 template <class E, typename OutT, int D>
 hipError_t launch_decode_g(const DecParams& p, int G, dim3 grid, hipStream_t s) {
-  switch (G) {
-    case 1: hipLaunchKernelGGL((decode_kernel<E, OutT, D, 1>), grid, dim3(kDecThreads), 0, s, p); break;
-    case 2: hipLaunchKernelGGL((decode_kernel<E, OutT, D, 2>), grid, dim3(kDecThreads), 0, s, p); break;
-    case 4: hipLaunchKernelGGL((decode_kernel<E, OutT, D, 4>), grid, dim3(kDecThreads), 0, s, p); break;
-    case 8: hipLaunchKernelGGL((decode_kernel<E, OutT, D, 8>), grid, dim3(kDecThreads), 0, s, p); break;
-    default: return hipErrorInvalidValue;
-  }
+  if (G <= 1)
+    hipLaunchKernelGGL((decode_kernel<E, OutT, D, 1>), grid, dim3(kDecThreads), 0, s, p);
+  else if (G <= 2)
+    hipLaunchKernelGGL((decode_kernel<E, OutT, D, 2>), grid, dim3(kDecThreads), 0, s, p);
+  else if (G <= 4)
+    hipLaunchKernelGGL((decode_kernel<E, OutT, D, 4>), grid, dim3(kDecThreads), 0, s, p);
+  else if (G <= 8)
+    hipLaunchKernelGGL((decode_kernel<E, OutT, D, 8>), grid, dim3(kDecThreads), 0, s, p);
+  else if (G <= 16)
+    hipLaunchKernelGGL((decode_kernel<E, OutT, D, 16>), grid, dim3(kDecThreads), 0, s, p);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
@@ -505,6 +513,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   p.B = a.B; p.H = a.H; p.Hkv = a.Hkv;
   p.max_pages = a.max_pages; p.num_pages = a.num_pages;
   p.num_splits = a.num_splits; p.max_splits = a.max_splits;
+  p.group = a.H / a.Hkv;
   p.c = a.scale * kLog2e;
   p.window = a.window;
   p.softcap_on = a.softcap > 0.f ? 1 : 0;

@@ -41,7 +41,8 @@
  *     their output buffers do not overlap.
  *   - Every argument is validated on the host BEFORE anything is launched.
  *     A call that returns an error status has enqueued no work and has not
- *     touched any buffer. FA_ERR_HIP reports a failed launch
+ *     touched any buffer. Sizes whose launch would exceed HIP's limit of
+ *     2^32 - 1 threads along a grid dimension return FA_ERR_BAD_SHAPE. FA_ERR_HIP reports a failed launch
  *     (hipGetLastError after the launch); no C++ exception crosses the ABI.
  *   - Softmax scale is explicit. LSE is the natural-log log-sum-exp of the
  *     scaled scores over the visible keys, m + ln(l) ("3.4 Attention
@@ -72,7 +73,7 @@ typedef enum {
 typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
 
 /* Largest number of key splits per sequence fa_decode_paged uses. */
-#define FA_MAX_SPLITS 16
+#define FA_MAX_SPLITS 64
 /* Token slots per KV page accepted by fa_decode_paged. */
 #define FA_PAGE_SIZE 16
 /* Largest number of key ranges fa_cascade splits the shared prefix into. */
@@ -207,25 +208,39 @@ fa_status fa_cascade(const void* Q, const int32_t* qo_indptr,
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * fa_decode_num_splits - the number of key chunks fa_decode_paged uses for a
- * sequence of seq_len tokens. num_splits > 0 forces that count;
- * num_splits == 0 picks ceil(seq_len / 256) clamped to [1, FA_MAX_SPLITS]:
- * chunks of at least 256 tokens, as many as allowed, so long and short
- * sequences alike spread over enough workgroups to keep HBM busy to the end
- * of the launch ("3.4 Attention Kernels", "In practice": the split count
- * follows from how long the context is). Returns -1 for invalid input.
- * Pure host function; the kernels evaluate the same rule on the device.
+ * The split plan of fa_decode_paged ("3.4 Attention Kernels", sections
+ * "Decode attention and Flash-Decoding", "Worked example" and "In practice":
+ * the keys of a sequence are split so that enough workgroups stream the cache
+ * to fill the GPU, the count chosen from the batch size, the head count and
+ * the context length).
+ *
+ * fa_decode_max_splits - the most chunks any sequence of a batch of B
+ * sequences with Hkv KV heads is cut into, which is also the number of
+ * partial slots per (sequence, head) in the workspace. num_splits > 0 forces
+ * that count; num_splits == 0 gives ceil(8192 / (B * Hkv)) clamped to
+ * [1, FA_MAX_SPLITS]: about 8192 (sequence, KV head, chunk) workgroups in all
+ * when every sequence is long (64 at batch 1 with 8 KV heads, 16 at 64
+ * sequences, 4 at 256). Returns -1 for invalid input.
+ *
+ * fa_decode_num_splits - the number of key chunks a sequence with seq_len
+ * visible tokens gets in that batch: num_splits > 0 forces it; num_splits ==
+ * 0 gives ceil(seq_len / 256) clamped to [1, fa_decode_max_splits(B, Hkv, 0)],
+ * so no chunk is shorter than 256 tokens unless the sequence is. Chunks are
+ * near-equal and page-aligned. Returns -1 for invalid input (B, Hkv >= 1).
+ *
+ * Pure host functions; the kernels evaluate the same rule on the device.
  */
-int fa_decode_num_splits(int seq_len, int num_splits);
+int fa_decode_max_splits(int B, int Hkv, int num_splits);
+int fa_decode_num_splits(int seq_len, int B, int Hkv, int num_splits);
 
 /*
  * fa_decode_workspace_size - bytes of device workspace fa_decode_paged needs
- * for B sequences of H query heads of dimension d with up to max_splits
- * chunks per sequence (use FA_MAX_SPLITS when num_splits == 0).
- * The workspace holds one fp32 partial (o[d], lse) per (b, h, chunk).
+ * for B sequences of H query heads (Hkv KV heads) of dimension d and the
+ * given num_splits (0 = automatic): one fp32 partial (o[d], lse) per
+ * (b, h, slot), fa_decode_max_splits(B, Hkv, num_splits) slots each.
  * Returns 0 for invalid sizes.
  */
-size_t fa_decode_workspace_size(int B, int H, int d, int max_splits);
+size_t fa_decode_workspace_size(int B, int H, int Hkv, int d, int num_splits);
 
 /*
  * fa_decode_paged - one query token per sequence against a paged KV cache.
@@ -252,14 +267,14 @@ size_t fa_decode_workspace_size(int B, int H, int d, int max_splits);
  *   seq_lens     [B]                     int32      device memory
  *   O            [B, H, d]                          out_dtype (dtype or FA_F32)
  *   LSE          [B, H]                  float
- *   workspace    >= fa_decode_workspace_size(B, H, d, S) bytes, S = num_splits
- *                or FA_MAX_SPLITS when num_splits == 0; device memory,
- *                contents on entry are ignored, on exit unspecified.
+ *   workspace    >= fa_decode_workspace_size(B, H, Hkv, d, num_splits) bytes
+ *                of device memory (may be NULL when that count of slots is
+ *                1); contents on entry are ignored, on exit unspecified.
  *
  * Supported: dtype in {FA_F16, FA_BF16}; d in {64, 128}; page_size ==
  * FA_PAGE_SIZE; 0 <= num_splits <= FA_MAX_SPLITS; H % Hkv == 0 and
- * H / Hkv in {1, 2, 4, 8}; B <= 65535. A sequence of length 0 gets O = 0,
- * LSE = -inf.
+ * 1 <= H / Hkv <= 16 (a larger group returns FA_ERR_UNSUPPORTED);
+ * B, Hkv <= 65535. A sequence of length 0 gets O = 0, LSE = -inf.
  * Device-side contract (not checkable on the host without a sync):
  * 0 <= seq_lens[b] <= max_pages_per_seq * page_size and every used table
  * entry lies in [0, num_pages). A sequence that breaks it is not read out of
@@ -288,8 +303,9 @@ fa_status fa_decode_paged(const void* q, const void* K_pool,
  *   softcap > 0  each scaled score x = scale * q.k is replaced by
  *                softcap * tanh(x / softcap) before the softmax; LSE is the
  *                log-sum-exp of the capped scores. softcap == 0 disables it.
- * The chunk count of a sequence is fa_decode_num_splits(v, num_splits) with
- * v = the number of visible tokens (min(seq_lens[b], window) for window > 0).
+ * The chunk count of a sequence is fa_decode_num_splits(v, B, Hkv, num_splits)
+ * with v = the number of visible tokens (min(seq_lens[b], window) for
+ * window > 0).
  * Everything else (layouts, workspace, support, contract, NaN on contract
  * violation) is as for fa_decode_paged; window < 0 or a negative or
  * non-finite softcap returns FA_ERR_BAD_ARG. With window == 0 and

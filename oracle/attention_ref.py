@@ -26,8 +26,9 @@ Readings taken where the pages leave a point open:
   * Layout [batch, seq, heads, d] for Q/K/V/O ("3.4 Attention Kernels",
     "Paged and ragged layouts"), LSE as [batch, heads, seq].
   * Causal alignment is bottom-right: key j is visible to query i iff
-    j <= i + (Nk - Nq). This is the `tril(..., k=len(K)-N)` of the page's
-    `naive_attention`; it equals top-left alignment when Nq == Nk.
+    j <= i + (Nk - Nq), the alignment of the mask in the page's NumPy naive
+    attention ("3.4 Attention Kernels", section "Code"); it equals top-left
+    alignment when Nq == Nk.
   * Grouped-query heads are contiguous groups: query head h reads KV head
     h // (H // Hkv) ("3.4 Attention Kernels", "Decode attention and
     Flash-Decoding", the GQA paragraph).
@@ -93,9 +94,9 @@ def _f64(x) -> np.ndarray:
 def causal_visible(q_idx: np.ndarray, n_keys: int, offset: int) -> np.ndarray:
     """Boolean [len(q_idx), n_keys]: key j visible to query i iff j <= i + offset.
 
-    offset = Nk - Nq (bottom-right alignment), as in the
-    `tril(ones((N, len(K))), k=len(K) - N)` mask of "3.4 Attention Kernels",
-    section "Code" (`naive_attention`).
+    offset = Nk - Nq: the bottom-right aligned causal mask, the diagonal
+    ending at the last query and the last key, as the page's NumPy naive
+    attention builds it ("3.4 Attention Kernels", section "Code").
     """
     keys = np.arange(n_keys)[None, :]
     return keys <= (q_idx[:, None] + offset)

@@ -64,6 +64,12 @@ def assert_lowp_out(name, got_lowp: torch.Tensor, ref):
     assert not bad.any(), f"{name}: {bad.sum()} values outside 1e-2 + half ulp"
 
 
+def ulp_f32(x):
+    """Spacing of float32 values at |x| (the distance to the next one up)."""
+    a = np.abs(np.asarray(x, np.float64)).astype(np.float32)
+    return (np.nextafter(a, np.float32(np.inf)) - a).astype(np.float64)
+
+
 def assert_lse(name, got, ref, tol=LSE_MAX):
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
@@ -72,3 +78,18 @@ def assert_lse(name, got, ref, tol=LSE_MAX):
     assert np.all(np.isfinite(got[fin])), f"{name}: non-finite LSE"
     err = report(name + " lse", got[fin], ref[fin])
     assert err.max(initial=0) <= tol, f"{name}: LSE err {err.max():.3e} > {tol}"
+
+
+def assert_lse_ulp(name, got, ref, ulps=2):
+    """LSE within max(1e-4, `ulps` float32 ulps of |LSE|) of the exact value,
+    per element: an fp32 result of magnitude beyond a few thousand cannot
+    hold 1e-4 absolute (ulp_f32(3000) is 2.4e-4), below that 1e-4 binds."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert np.array_equal(np.isneginf(got), np.isneginf(ref)), f"{name}: -inf rows differ"
+    fin = np.isfinite(ref)
+    assert np.all(np.isfinite(got[fin])), f"{name}: non-finite LSE"
+    err = report(name + " lse", got[fin], ref[fin])
+    tol = np.maximum(LSE_MAX, ulps * ulp_f32(ref[fin]))
+    bad = err > tol
+    assert not bad.any(), f"{name}: {bad.sum()} LSE values beyond max(1e-4, {ulps} ulp)"

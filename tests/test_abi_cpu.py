@@ -58,6 +58,10 @@ FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails val
     (dict(scale=float("nan")), ARG), (dict(ind=BF16, outd=F16), UNSUP),
     (dict(ind=F32, outd=BF16), UNSUP),
     (dict(B=1 << 14, Nq=1 << 14, H=16, d=128), SHAPE),
+    # 2^24 workgroups of 512 threads: more than 2^32 - 1 threads along x
+    (dict(B=1 << 24, Nq=1, Nk=1, d=64), SHAPE),
+    (dict(B=(1 << 24) - 1, Nq=1, Nk=1, d=64, ind=F32, outd=F32), NULL),
+    (dict(B=1 << 24, Nq=1, Nk=1, d=64, ind=F32, outd=F32), SHAPE),
     (dict(), NULL), (dict(B=0), OK), (dict(Nq=0), OK),
 ])
 def test_forward_validation(kw, status):
@@ -93,10 +97,12 @@ def dec(B=2, H=8, Hkv=2, d=128, page=16, max_pages=4, num_pages=8, scale=0.1, sp
 @pytest.mark.parametrize("kw,status", [
     (dict(B=-1), SHAPE), (dict(H=0), SHAPE), (dict(H=6, Hkv=4), SHAPE),
     (dict(max_pages=0), SHAPE), (dict(num_pages=0), SHAPE), (dict(page=0), SHAPE),
-    (dict(splits=-1), ARG), (dict(splits=17), ARG), (dict(dt=9), ARG),
+    (dict(splits=-1), ARG), (dict(splits=65), ARG), (dict(dt=9), ARG),
     (dict(scale=0.0), ARG), (dict(d=96), UNSUP), (dict(page=8), UNSUP),
-    (dict(page=32), UNSUP), (dict(dt=F32, outd=F32), UNSUP), (dict(H=48, Hkv=3), UNSUP),
-    (dict(H=32, Hkv=2), UNSUP), (dict(dt=F16, outd=BF16), UNSUP),
+    (dict(page=32), UNSUP), (dict(dt=F32, outd=F32), UNSUP), (dict(H=51, Hkv=3), UNSUP),
+    (dict(H=34, Hkv=2), UNSUP), (dict(H=32, Hkv=1), UNSUP), (dict(dt=F16, outd=BF16), UNSUP),
+    (dict(H=48, Hkv=3), NULL), (dict(H=32, Hkv=2), NULL), (dict(H=18, Hkv=3), NULL),
+    (dict(splits=64), NULL),
     (dict(B=70000), SHAPE), (dict(), NULL), (dict(B=0), OK),
 ])
 def test_decode_validation(kw, status):
@@ -112,7 +118,7 @@ def dec_ex(window=0, softcap=0.0, B=2, H=8, Hkv=2, d=128, page=16, max_pages=4, 
 @pytest.mark.parametrize("kw,status", [
     (dict(window=-1), ARG), (dict(softcap=-1.0), ARG), (dict(softcap=float("nan")), ARG),
     (dict(softcap=float("inf")), ARG), (dict(window=5, B=0), OK), (dict(softcap=30.0), NULL),
-    (dict(window=4096, softcap=50.0, d=96), UNSUP), (dict(window=3, splits=17), ARG),
+    (dict(window=4096, softcap=50.0, d=96), UNSUP), (dict(window=3, splits=65), ARG),
     (dict(B=-1, window=1), SHAPE), (dict(window=1, B=0), OK),
 ])
 def test_decode_ex_validation(kw, status):
@@ -121,7 +127,7 @@ def test_decode_ex_validation(kw, status):
 
 def test_decode_ex_workspace_checks():
     p = [FAKE] * 7
-    need = fa.decode_workspace_size(2, 8, 128, 16)
+    need = fa.decode_workspace_size(2, 8, 2, 128, 0)
     assert dec_ex(window=100, ptrs=p, ws=None, ws_bytes=need) == WS
     assert dec_ex(window=100, ptrs=p, ws=FAKE, ws_bytes=need - 1) == WS
 
@@ -138,7 +144,7 @@ def test_decode_graph_validation_before_any_hip_call():
     assert create(ctypes.byref(h), window=-1) == ARG
     assert h.value is None
     assert create(ctypes.byref(h), softcap=float("nan")) == ARG
-    assert create(ctypes.byref(h), splits=17) == ARG
+    assert create(ctypes.byref(h), splits=65) == ARG
     assert create(ctypes.byref(h), ptrs=[None] * 7) == NULL
     assert create(ctypes.byref(h), ws=None, ws_bytes=0) == WS
     assert lib.fa_decode_graph_launch(None, None) == NULL
@@ -229,30 +235,49 @@ def test_cascade_pointer_and_workspace_checks():
 
 def test_decode_workspace_checks():
     p = [FAKE] * 7
-    need = fa.decode_workspace_size(2, 8, 128, 16)
+    need = fa.decode_workspace_size(2, 8, 2, 128, 0)
     assert need > 0
     assert dec(ptrs=p, ws=None, ws_bytes=need) == WS
     assert dec(ptrs=p, ws=FAKE, ws_bytes=need - 1) == WS
-    need4 = fa.decode_workspace_size(2, 8, 128, 4)
+    need4 = fa.decode_workspace_size(2, 8, 2, 128, 4)
     assert need4 < need
     assert dec(ptrs=p, splits=4, ws=FAKE, ws_bytes=need4 - 4) == WS
 
 
 def test_split_rule_and_workspace_size():
-    assert [fa.decode_num_splits(n) for n in (0, 1, 256, 257, 1024, 2049, 3840, 4096, 4097, 10**6)] \
-        == [1, 1, 1, 2, 4, 9, 15, 16, 16, 16]
-    assert [fa.decode_num_splits(100, s) for s in range(1, 17)] == list(range(1, 17))
-    assert fa.decode_num_splits(-1) == -1 and fa.decode_num_splits(5, 17) == -1
+    # the cap: ceil(8192 / (B * Hkv)) clamped to [1, 64]
+    assert [fa.decode_max_splits(B, 8) for B in (1, 2, 4, 8, 16, 32, 64, 128, 256, 1024, 2048)] \
+        == [64, 64, 64, 64, 64, 32, 16, 8, 4, 1, 1]
+    assert fa.decode_max_splits(3, 5) == 64 and fa.decode_max_splits(100, 1) == 64
+    assert fa.decode_max_splits(100, 2) == 41 and fa.decode_max_splits(0, 8) == 64
+    assert [fa.decode_max_splits(64, 8, s) for s in (1, 7, 64)] == [1, 7, 64]
+    assert fa.decode_max_splits(1, 0) == -1 and fa.decode_max_splits(1, 8, 65) == -1
+    # per sequence: ceil(len / 256) under the cap
+    lens = (0, 1, 256, 257, 1024, 2049, 3840, 4096, 4097, 16384, 16385, 10**6)
+    assert [fa.decode_num_splits(n, 64, 8) for n in lens] == \
+        [1, 1, 1, 2, 4, 9, 15, 16, 16, 16, 16, 16]
+    assert [fa.decode_num_splits(n, 1, 8) for n in lens] == \
+        [1, 1, 1, 2, 4, 9, 15, 16, 17, 64, 64, 64]
+    assert fa.decode_num_splits(32768, 1, 8) == 64 and fa.decode_num_splits(32768, 256, 8) == 4
+    assert [fa.decode_num_splits(100, 64, 8, s) for s in range(1, 65)] == list(range(1, 65))
+    assert fa.decode_num_splits(-1, 1, 1) == -1 and fa.decode_num_splits(5, 1, 1, 65) == -1
+    assert fa.decode_num_splits(5, 0, 1) == -1
     # fp32 o-partials, 256-byte aligned, followed by the fp32 lse-partials
-    assert fa.decode_workspace_size(64, 32, 128, 16) == 64 * 32 * 16 * 128 * 4 + 64 * 32 * 16 * 4
-    assert fa.decode_workspace_size(1, 1, 1, 1) == 256 + 4
-    assert fa.decode_workspace_size(1, 1, 1, 0) == 0 and fa.decode_workspace_size(1, 1, 1, 17) == 0
+    assert fa.decode_workspace_size(64, 32, 8, 128, 0) == \
+        64 * 32 * 16 * 128 * 4 + 64 * 32 * 16 * 4
+    assert fa.decode_workspace_size(1, 32, 8, 128, 0) == 32 * 64 * 128 * 4 + 32 * 64 * 4
+    assert fa.decode_workspace_size(1, 1, 1, 1, 1) == 256 + 4
+    assert fa.decode_workspace_size(1, 1, 1, 1, -1) == 0
+    assert fa.decode_workspace_size(1, 1, 1, 1, 65) == 0
+    assert fa.decode_workspace_size(1, 3, 2, 1, 0) == 0
 
 
 @pytest.mark.parametrize("args,status", [
     ((-1, 2, 64, F32), SHAPE), ((4, 0, 64, F32), SHAPE), ((4, 1025, 64, F32), SHAPE),
     ((4, 2, 0, F32), SHAPE), ((4, 2, 1025, F32), SHAPE), ((4, 2, 64, 5), ARG),
     ((4, 2, 64, F32), NULL), ((0, 2, 64, F32), OK),
+    # (R + 3) / 4 workgroups of 256 threads: beyond 2^32 - 1 threads along x
+    (((1 << 26) - 3, 1, 1, F32), SHAPE), (((1 << 26) - 4, 1, 1, F32), NULL),
 ])
 def test_merge_validation(args, status):
     R, S, d, outd = args

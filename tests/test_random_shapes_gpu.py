@@ -2,7 +2,8 @@
 and the paged decode, each compared with the float64 oracle.
 
 The shapes are drawn once, at import, from a fixed seed: head counts and
-group sizes, head dims, query and key lengths that are and are not multiples
+group sizes (powers of two and not, up to one KV head for 32 query heads),
+head dims, query and key lengths that are and are not multiples
 of the 64-key tile or of a wave's 32 rows (including fewer keys than queries,
 fewer than one tile, and none at all), causal or not, 16-bit and fp32 inputs.
 The sizes stay small enough for the oracle to finish in a second or two.
@@ -35,7 +36,7 @@ def _draw_dense(n, seed):
     cases = []
     for i in range(n):
         hkv = int(rng.choice([1, 2, 3]))
-        g = int(rng.choice([1, 2, 4, 8]))
+        g = int(rng.choice([1, 2, 3, 4, 6, 8, 16, 32]))
         d = int(rng.choice([64, 128]))
         dt = str(rng.choice(["bf16", "f16", "bf16", "f16", "f32"]))
         nq = int(rng.integers(1, 520))
@@ -51,7 +52,7 @@ def _draw_paged(n, seed):
     cases = []
     for i in range(n):
         hkv = int(rng.choice([1, 2, 4]))
-        g = int(rng.choice([1, 2, 4, 8]))
+        g = int(rng.choice([1, 2, 3, 4, 6, 8, 16, 32]))
         d = int(rng.choice([64, 128]))
         dt = str(rng.choice(["bf16", "f16"]))
         nseq = int(rng.integers(1, 6))
@@ -70,13 +71,13 @@ def _draw_decode(n, seed):
     cases = []
     for i in range(n):
         hkv = int(rng.choice([1, 2, 4, 8]))
-        g = int(rng.choice([1, 2, 4, 8]))
+        g = int(rng.choice([1, 2, 3, 4, 5, 6, 8, 16]))
         d = int(rng.choice([64, 128]))
         dt = str(rng.choice(["bf16", "f16"]))
         nseq = int(rng.integers(1, 9))
         lens = [[0, 1, int(rng.integers(1, 9000))][int(rng.choice(3, p=[0.05, 0.05, 0.9]))]
                 for _ in range(nseq)]
-        splits = int(rng.choice([0, 0, 1, int(rng.integers(2, 17))]))
+        splits = int(rng.choice([0, 0, 1, int(rng.integers(2, 65))]))
         cases.append((hkv * g, hkv, d, dt, lens, splits, 3000 + i))
     return cases
 
