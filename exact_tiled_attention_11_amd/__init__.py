@@ -47,6 +47,8 @@ _SIGNATURES = {
                              _I, _I, _P, ctypes.c_size_t, _P]),
     "fa_decode_paged_ex": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F,
                                 _I, _I, _F, _I, _I, _P, ctypes.c_size_t, _P]),
+    "fa_decode_paged_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I,
+                                     _F, _I, _I, _F, _I, _I, _P]),
     "fa_decode_graph_create": (_I, [ctypes.POINTER(ctypes.c_void_p), _P, _P, _P, _P, _P, _P,
                                     _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _F, _I, _I, _P,
                                     ctypes.c_size_t]),
@@ -279,6 +281,35 @@ def decode_paged_ex(q, k_pool, v_pool, block_table, seq_lens, window: int = 0,
     logit soft-capping (scaled scores x -> softcap*tanh(x/softcap), 0 = off)."""
     return _decode("fa_decode_paged_ex", q, k_pool, v_pool, block_table, seq_lens, scale,
                    num_splits, out_dtype, out, lse, workspace, (int(window), float(softcap)))
+
+
+def decode_paged_noalloc(q, k_pool, v_pool, block_table, seq_lens, window: int = 0,
+                         softcap: float = 0.0, scale: float | None = None, num_splits: int = 0,
+                         out_dtype=None, out=None, lse=None):
+    """decode_paged_ex whose partials live in the library's own per-device scratch
+    buffer (fa_decode_paged_noalloc): no workspace. With `out` and `lse` given,
+    nothing is allocated at all. Calls that overlap in time on one device race."""
+    if q.dim() != 3 or k_pool.dim() != 4 or v_pool.shape != k_pool.shape:
+        raise ValueError("expected q [B,H,d] and pools [P,page,Hkv,d]")
+    B, H, d = q.shape
+    num_pages, page, Hkv = k_pool.shape[0], k_pool.shape[1], k_pool.shape[2]
+    if block_table.dim() != 2 or block_table.shape[0] != B or tuple(seq_lens.shape) != (B,):
+        raise ValueError("block_table must be [B, max_pages] and seq_lens [B]")
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((B, H, d), dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    with torch.cuda.device(q.device):
+        st = lib().fa_decode_paged_noalloc(
+            _dev(q, "q"), _dev(k_pool, "k_pool", q.dtype), _dev(v_pool, "v_pool", q.dtype),
+            _dev(block_table, "block_table", torch.int32), _dev(seq_lens, "seq_lens", torch.int32),
+            _dev(out, "out", out_dtype), _dev(lse, "lse", torch.float32), B, H, Hkv, d, page,
+            block_table.shape[1], num_pages, scale, int(num_splits), int(window), float(softcap),
+            _code(q.dtype), _code(out_dtype), _stream(q.device))
+    _check(st, "fa_decode_paged_noalloc")
+    return out, lse
 
 
 class DecodeGraph:

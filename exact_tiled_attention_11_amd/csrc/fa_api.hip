@@ -64,6 +64,9 @@ const char* fa_status_string(fa_status s) {
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or smaller than required";
     case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported a launch failure";
     case FA_ERR_BAD_ARG: return "FA_ERR_BAD_ARG: an argument is out of range";
+    case FA_ERR_SCRATCH:
+      return "FA_ERR_SCRATCH: the sizes need more partial-result memory than the library's "
+             "fixed scratch buffer holds (use the entry point with a caller workspace)";
   }
   return "unknown fa_status";
 }
@@ -357,6 +360,29 @@ fa_status fa_decode_paged_ex(const void* q, const void* K_pool, const void* V_po
   return decode_impl(q, K_pool, V_pool, block_table, seq_lens, O, LSE, B, H, Hkv, d, page_size,
                      max_pages_per_seq, num_pages, scale, num_splits, window, softcap, dtype,
                      out_dtype, workspace, workspace_bytes, stream);
+}
+
+fa_status fa_decode_paged_noalloc(const void* q, const void* K_pool, const void* V_pool,
+                                  const int32_t* block_table, const int32_t* seq_lens, void* O,
+                                  float* LSE, int B, int H, int Hkv, int d, int page_size,
+                                  int max_pages_per_seq, int num_pages, float scale,
+                                  int num_splits, int window, float softcap, fa_dtype dtype,
+                                  fa_dtype out_dtype, void* stream) {
+  // Everything but the workspace is validated exactly as for
+  // fa_decode_paged_ex; the partials then go to the library's fixed buffer.
+  fa::DecodeArgs a;
+  bool empty;
+  fa_status st = decode_prepare(q, K_pool, V_pool, block_table, seq_lens, O, LSE, B, H, Hkv, d,
+                                page_size, max_pages_per_seq, num_pages, scale, num_splits,
+                                window, softcap, dtype, out_dtype, nullptr, 0, &a, &empty,
+                                /*check_workspace=*/false);
+  if (st != FA_OK || empty) return st;
+  if (fa_decode_workspace_size(B, H, Hkv, d, num_splits) > fa::kDecodeScratchBytes)
+    return FA_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (fa::decode_scratch(&ws) != hipSuccess) return FA_ERR_HIP;
+  set_partials(&a, ws);
+  return from_hip(fa::launch_decode(a, static_cast<hipStream_t>(stream)));
 }
 
 struct fa_decode_graph {

@@ -37,6 +37,8 @@
 // scaled score x becomes cap * tanh(x / cap) before the softmax).
 // Merge kernel, one wave per (sequence, head): M = max lse, weights e^(lse-M),
 // fixed summation order, no atomics.
+#include <mutex>
+
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
 #include "fa_split_rule.hpp"
@@ -496,7 +498,34 @@ hipError_t launch_decode_d(const DecParams& p, int D, int G, dim3 grid, hipStrea
                  : launch_decode_g<E, OutT, 128>(p, G, grid, s);
 }
 
+constexpr int kMaxDevices = 64;
+
 }  // namespace
+
+// Partial results of fa_decode_paged_noalloc, for callers that cannot
+// allocate: one buffer per device for the life of the process. Host code must
+// never pass this name to a kernel or a copy (in host code it is a stand-in,
+// not a device address); decode_scratch() hands out the device address.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   if (a.B == 0) return hipSuccess;

@@ -76,6 +76,12 @@ struct MergeArgs {
   const float* lse_extra = nullptr;  // [R]
 };
 
+// Size of the library's own partial-result buffer (fa_decode_paged_noalloc).
+constexpr size_t kDecodeScratchBytes = FA_NOALLOC_SCRATCH_BYTES;
+// Device address of that buffer on the current device (looked up once per
+// device, then cached).
+hipError_t decode_scratch(void** ptr);
+
 hipError_t launch_forward(const ForwardArgs& a, hipStream_t s);
 hipError_t launch_forward_paged(const ForwardPagedArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);

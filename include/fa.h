@@ -36,9 +36,10 @@
  *     FA_ERR_BAD_ARG); the kernels move them in 16-byte vectors.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Work is enqueued asynchronously on it; outputs are valid once the
- *     stream has been synchronised. The library holds no global mutable
- *     state, so calls on different streams may run concurrently provided
- *     their output buffers do not overlap.
+ *     stream has been synchronised. Apart from the one scratch buffer of
+ *     fa_decode_paged_noalloc, the library holds no global mutable state, so
+ *     calls on different streams may run concurrently provided their output
+ *     buffers do not overlap.
  *   - Every argument is validated on the host BEFORE anything is launched.
  *     A call that returns an error status has enqueued no work and has not
  *     touched any buffer. Sizes whose launch would exceed HIP's limit of
@@ -67,7 +68,8 @@ typedef enum {
   FA_ERR_UNSUPPORTED = 3, /* valid but not implemented (head dim, dtype...) */
   FA_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than required        */
   FA_ERR_HIP = 5,         /* the HIP runtime reported a launch failure      */
-  FA_ERR_BAD_ARG = 6      /* a non-size argument is out of range            */
+  FA_ERR_BAD_ARG = 6,     /* a non-size argument is out of range            */
+  FA_ERR_SCRATCH = 7      /* more partials than the fixed scratch buffer    */
 } fa_status;
 
 typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
@@ -320,6 +322,38 @@ fa_status fa_decode_paged_ex(const void* q, const void* K_pool,
                              fa_dtype dtype, fa_dtype out_dtype,
                              void* workspace, size_t workspace_bytes,
                              void* stream);
+
+/*
+ * fa_decode_paged_noalloc - fa_decode_paged_ex for callers that cannot
+ * allocate device memory or pass a workspace: code being recorded into a HIP
+ * graph, tight serving loops, harnesses that forbid allocation.
+ *
+ * Same arguments, validation, arithmetic and results as fa_decode_paged_ex
+ * (bit for bit), without the workspace: the per-chunk partials go to a buffer
+ * of FA_NOALLOC_SCRATCH_BYTES that the library holds on each device from its
+ * first call there until the process ends (a file-scope device array; its
+ * device address is looked up once per device). The call itself allocates
+ * nothing. Every partial the merge reads is written by the same call first,
+ * so nothing needs clearing between calls.
+ *
+ * Limit: fa_decode_workspace_size(B, H, Hkv, d, num_splits) must not exceed
+ * FA_NOALLOC_SCRATCH_BYTES, else FA_ERR_SCRATCH (nothing launched). The
+ * 64-sequence, 32/8-head, d = 128 batch with automatic splits needs 16.8 MB.
+ *
+ * Runs on the current HIP device. All calls on one device share its buffer:
+ * calls that overlap in time on one device (different streams, threads, or
+ * graph replays running together) race and give wrong results; calls on one
+ * stream are ordered and safe.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (32u << 20)
+fa_status fa_decode_paged_noalloc(const void* q, const void* K_pool,
+                                  const void* V_pool, const int32_t* block_table,
+                                  const int32_t* seq_lens, void* O, float* LSE,
+                                  int B, int H, int Hkv, int d, int page_size,
+                                  int max_pages_per_seq, int num_pages,
+                                  float scale, int num_splits, int window,
+                                  float softcap, fa_dtype dtype,
+                                  fa_dtype out_dtype, void* stream);
 
 /*
  * A decode step recorded once and replayed with one launch.

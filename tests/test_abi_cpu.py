@@ -12,7 +12,7 @@ import exact_tiled_attention_11_amd as fa
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fa.h")
 
-OK, NULL, SHAPE, UNSUP, WS, HIP, ARG = range(7)
+OK, NULL, SHAPE, UNSUP, WS, HIP, ARG, SCRATCH = range(8)
 F32, F16, BF16 = 0, 1, 2
 
 
@@ -36,7 +36,7 @@ def test_binding_covers_every_declared_function():
 
 
 def test_status_strings_and_version():
-    for s in range(7):
+    for s in range(8):
         assert fa.status_string(s).startswith("FA_")
     assert fa.status_string(99) == "unknown fa_status"
     assert re.fullmatch(r"\d+\.\d+\.\d+", fa.version())
@@ -310,3 +310,25 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def dec_noalloc(B=2, H=8, Hkv=2, d=128, page=16, max_pages=4, num_pages=8, scale=0.1, splits=0,
+                window=0, softcap=0.0, dt=BF16, outd=BF16, ptrs=(None,) * 7):
+    return fa.lib().fa_decode_paged_noalloc(*ptrs, B, H, Hkv, d, page, max_pages, num_pages,
+                                            scale, splits, window, softcap, dt, outd, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), SHAPE), (dict(splits=65), ARG), (dict(window=-1), ARG),
+    (dict(softcap=float("nan")), ARG), (dict(d=96), UNSUP), (dict(H=34, Hkv=2), UNSUP),
+    (dict(B=0), OK), (dict(), NULL),
+])
+def test_decode_noalloc_validation(kw, status):
+    assert dec_noalloc(**kw) == status
+
+
+def test_decode_noalloc_rejects_more_partials_than_its_scratch():
+    p = [FAKE] * 7
+    # 64 sequences of 128 query heads over 8 KV heads need 67 MB of partials
+    assert fa.decode_workspace_size(64, 128, 8, 128, 0) > 32 << 20
+    assert dec_noalloc(B=64, H=128, Hkv=8, max_pages=2048, num_pages=1 << 16, ptrs=p) == SCRATCH
