@@ -133,8 +133,9 @@ def bench_decode_variants(torch, fa, inputs, pi, dev, lens, dp, steps):
     window, cap = 4096, 50.0
     vis = np.minimum(lens, window).astype(np.float64)
     kv = float(vis.sum()) * dp["Hkv"] * dp["d"] * 2 * 2
-    ws = torch.empty(fa.decode_workspace_size(dp["B"], dp["H"], dp["Hkv"], dp["d"]),
-                     dtype=torch.uint8, device="cuda")
+    ws = torch.empty(fa.decode_workspace_size(dp["B"], dp["H"], dp["Hkv"], dp["d"],
+                                              dev["t"].shape[1], window), dtype=torch.uint8,
+                     device="cuda")
     od = torch.empty_like(dev["q"])
     ld = torch.empty((dp["B"], dp["H"]), dtype=torch.float32, device="cuda")
 
@@ -204,8 +205,8 @@ def bench_decode_batch1(torch, fa, inputs, reps=20, copies=4):
     out = {"workload": "decode batch 1, 32768 tokens, h32/kv8, d128, bf16, 16-token pages",
            "kv_bytes": kv, "caches_rotated": copies}
     for splits in (0, 16, 32, 64):
-        ws = torch.empty(fa.decode_workspace_size(1, H, Hkv, d, splits), dtype=torch.uint8,
-                         device="cuda")
+        ws = torch.empty(fa.decode_workspace_size(1, H, Hkv, d, devs[0]["t"].shape[1], 0,
+                                                  splits), dtype=torch.uint8, device="cuda")
         it = [0]
 
         def run():
@@ -218,7 +219,8 @@ def bench_decode_batch1(torch, fa, inputs, reps=20, copies=4):
         ms = time_steps(torch, run, reps)
         gbs = kv / (ms * 1e-3) / 1e9
         key = "auto" if splits == 0 else f"splits_{splits}"
-        out[key] = {"splits": fa.decode_num_splits(L, 1, Hkv, splits), "us_mean": ms * 1e3,
+        out[key] = {"splits": int(fa.decode_plan([L], Hkv, devs[0]["t"].shape[1], 0, splits)[0]),
+                    "us_mean": ms * 1e3,
                     "value": gbs, "unit": "GB/s", "frac_hbm": gbs / HBM_PEAK_GBPS}
     del devs
     torch.cuda.empty_cache()
@@ -236,8 +238,8 @@ def bench_decode_graph(torch, fa, inputs, dev, dp, n=200):
                 t=spi.block_table.cuda(), s=spi.seq_lens.cuda())
     for name, d in (("b64_h32_kv8_paged", dev), ("b1_len1024", sdev)):
         B, H, hd = d["q"].shape
-        ws = torch.empty(fa.decode_workspace_size(B, H, d["k"].shape[2], hd), dtype=torch.uint8,
-                         device="cuda")
+        ws = torch.empty(fa.decode_workspace_size(B, H, d["k"].shape[2], hd, d["t"].shape[1]),
+                         dtype=torch.uint8, device="cuda")
         o = torch.empty_like(d["q"])
         lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
         g = fa.DecodeGraph(d["q"], d["k"], d["v"], d["t"], d["s"], out=o, lse=lse, workspace=ws)
@@ -397,7 +399,7 @@ def bench_cascade(torch, fa, inputs, reps=10):
         fa.cascade(q, ind, kp, vp, ppd, P, bt, kl, 1, causal=True, out=o, lse=lse, workspace=ws)
     full = torch.cat([prefix_pages.repeat(B, 1), ri.block_table], dim=1).cuda()
     full_lens = (ri.kv_lens + P).cuda()
-    dws = torch.empty(fa.decode_workspace_size(B, H, Hkv, d), dtype=torch.uint8,
+    dws = torch.empty(fa.decode_workspace_size(B, H, Hkv, d, full.shape[1]), dtype=torch.uint8,
                       device="cuda")
     o2 = torch.empty_like(o)
     l2 = torch.empty_like(lse)
@@ -507,8 +509,8 @@ def main():
         dt_, ds_ = pi.block_table.to(dev), pi.seq_lens.to(dev)
         od = torch.empty_like(dq)
         lsed = torch.empty((dp["B"], dp["H"]), dtype=torch.float32, device=dev)
-        ws = torch.empty(fa.decode_workspace_size(dp["B"], dp["H"], dp["Hkv"], dp["d"]),
-                         dtype=torch.uint8, device=dev)
+        ws = torch.empty(fa.decode_workspace_size(dp["B"], dp["H"], dp["Hkv"], dp["d"],
+                                                  dt_.shape[1]), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     def step(ev=None):

@@ -17,7 +17,7 @@ import os
 import torch
 
 __all__ = [
-    "FAError", "forward", "decode_paged", "merge_partials", "decode_num_splits",
+    "FAError", "forward", "decode_paged", "merge_partials", "decode_plan",
     "decode_max_splits", "decode_workspace_size", "lib", "LIB_PATH", "MAX_SPLITS", "PAGE_SIZE",
     "version",
 ]
@@ -40,9 +40,9 @@ _SIGNATURES = {
     "fa_cascade_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "fa_cascade": (_I, [_P, _P, _P, _P, _P, _I, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I,
                         _I, _I, _F, _I, _I, _I, _P, ctypes.c_size_t, _P]),
-    "fa_decode_max_splits": (_I, [_I, _I, _I]),
-    "fa_decode_num_splits": (_I, [_I, _I, _I, _I]),
-    "fa_decode_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
+    "fa_decode_max_splits": (_I, [_I, _I, _I, _I, _I]),
+    "fa_decode_plan": (_I, [_P, _I, _I, _I, _I, _I, _P]),
+    "fa_decode_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I, _I, _I, _I]),
     "fa_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I,
                              _I, _I, _P, ctypes.c_size_t, _P]),
     "fa_decode_paged_ex": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F,
@@ -221,18 +221,30 @@ def cascade_workspace_size(total_q: int, H: int, d: int, num_splits: int) -> int
     return int(lib().fa_cascade_workspace_size(total_q, H, d, num_splits))
 
 
-def decode_max_splits(B: int, Hkv: int, num_splits: int = 0) -> int:
-    """Most key chunks a sequence of a B-sequence batch gets (partial slots per head)."""
-    return lib().fa_decode_max_splits(int(B), int(Hkv), int(num_splits))
+def decode_max_splits(B: int, Hkv: int, max_pages_per_seq: int, window: int = 0,
+                      num_splits: int = 0) -> int:
+    """Partial slots per (sequence, head): the most key chunks any sequence can get."""
+    return lib().fa_decode_max_splits(int(B), int(Hkv), int(max_pages_per_seq), int(window),
+                                      int(num_splits))
 
 
-def decode_num_splits(seq_len: int, B: int, Hkv: int, num_splits: int = 0) -> int:
-    """Key chunks of a sequence with seq_len visible tokens in a B-sequence batch."""
-    return lib().fa_decode_num_splits(int(seq_len), int(B), int(Hkv), int(num_splits))
+def decode_plan(seq_lens, Hkv: int, max_pages_per_seq: int, window: int = 0,
+                num_splits: int = 0):
+    """The decode's split plan for a host list of sequence lengths: chunks per sequence."""
+    import numpy as np
+    lens = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    out = np.zeros(lens.shape[0], dtype=np.int32)
+    st = lib().fa_decode_plan(lens.ctypes.data if lens.size else None, int(lens.shape[0]),
+                              int(Hkv), int(max_pages_per_seq), int(window), int(num_splits),
+                              out.ctypes.data if out.size else None)
+    _check(st, "fa_decode_plan")
+    return out
 
 
-def decode_workspace_size(B: int, H: int, Hkv: int, d: int, num_splits: int = 0) -> int:
+def decode_workspace_size(B: int, H: int, Hkv: int, d: int, max_pages_per_seq: int,
+                          window: int = 0, num_splits: int = 0) -> int:
     return int(lib().fa_decode_workspace_size(int(B), int(H), int(Hkv), int(d),
+                                              int(max_pages_per_seq), int(window),
                                               int(num_splits)))
 
 
@@ -250,8 +262,10 @@ def _decode(entry, q, k_pool, v_pool, block_table, seq_lens, scale, num_splits, 
     if lse is None:
         lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    S = decode_max_splits(B, Hkv, num_splits) if B > 0 else 1
-    need = decode_workspace_size(B, H, Hkv, d, num_splits) if B > 0 else 0
+    window = extra[0] if extra else 0
+    S = decode_max_splits(B, Hkv, block_table.shape[1], window, num_splits) if B > 0 else 1
+    need = decode_workspace_size(B, H, Hkv, d, block_table.shape[1], window, num_splits) \
+        if B > 0 else 0
     if workspace is None and S > 1 and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
@@ -335,8 +349,9 @@ class DecodeGraph:
                                                            device=q.device)
         self.lse = lse if lse is not None else torch.empty((B, H), dtype=torch.float32,
                                                            device=q.device)
-        S = decode_max_splits(B, Hkv, num_splits) if B > 0 else 1
-        need = decode_workspace_size(B, H, Hkv, d, num_splits) if B > 0 else 0
+        S = decode_max_splits(B, Hkv, block_table.shape[1], window, num_splits) if B > 0 else 1
+        need = decode_workspace_size(B, H, Hkv, d, block_table.shape[1], window, num_splits) \
+            if B > 0 else 0
         if workspace is None and S > 1 and need > 0:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
         self.workspace = workspace

@@ -21,6 +21,7 @@ constexpr int64_t kMaxThreadsX = (int64_t{1} << 32) - 1;
 constexpr int64_t kFwd16Threads = 512;   // 8 waves
 constexpr int64_t kFwd32Threads = 256;   // 4 waves
 constexpr int64_t kMergeRowsPerBlock = 4, kMergeThreads = 256;
+constexpr int64_t kDecodeThreads = 256;  // 4 waves
 bool grid_fits(int64_t workgroups, int64_t threads) {
   return workgroups >= 0 && workgroups <= kMaxThreadsX / threads;
 }
@@ -232,25 +233,34 @@ fa_status fa_cascade(const void* Q, const int32_t* qo_indptr, const void* K_pool
   return from_hip(fa::launch_merge(m, st));
 }
 
-int fa_decode_max_splits(int B, int Hkv, int num_splits) {
-  if (B < 0 || Hkv < 1 || num_splits < 0 || num_splits > FA_MAX_SPLITS) return -1;
-  return fa::decode_max_splits(B, Hkv, num_splits);
-}
-
-int fa_decode_num_splits(int seq_len, int B, int Hkv, int num_splits) {
-  if (seq_len < 0 || B < 1 || Hkv < 1 || num_splits < 0 || num_splits > FA_MAX_SPLITS)
-    return -1;
-  return fa::decode_splits(seq_len, fa::decode_max_splits(B, Hkv, num_splits), num_splits);
-}
-
-size_t fa_decode_workspace_size(int B, int H, int Hkv, int d, int num_splits) {
-  if (B < 0 || H < 1 || Hkv < 1 || H % Hkv != 0 || d < 1 || num_splits < 0 ||
+int fa_decode_max_splits(int B, int Hkv, int max_pages_per_seq, int window, int num_splits) {
+  if (B < 0 || Hkv < 1 || max_pages_per_seq < 1 || window < 0 || num_splits < 0 ||
       num_splits > FA_MAX_SPLITS)
-    return 0;
-  const int S = fa::decode_max_splits(B, Hkv, num_splits);
+    return -1;
+  return fa::decode_max_splits(B, Hkv, max_pages_per_seq, window, num_splits);
+}
+
+size_t fa_decode_workspace_size(int B, int H, int Hkv, int d, int max_pages_per_seq, int window,
+                                int num_splits) {
+  const int S = fa_decode_max_splits(B, Hkv, max_pages_per_seq, window, num_splits);
+  if (H < 1 || H % Hkv != 0 || d < 1 || S < 1) return 0;
   const size_t rows = static_cast<size_t>(B) * static_cast<size_t>(H) * S;
   const size_t o_bytes = (rows * static_cast<size_t>(d) * sizeof(float) + 255) / 256 * 256;
   return o_bytes + rows * sizeof(float);
+}
+
+fa_status fa_decode_plan(const int32_t* seq_lens_host, int B, int Hkv, int max_pages_per_seq,
+                         int window, int num_splits, int32_t* splits_out) {
+  if (B < 0 || Hkv < 1 || max_pages_per_seq < 1) return FA_ERR_BAD_SHAPE;
+  if (window < 0 || num_splits < 0 || num_splits > FA_MAX_SPLITS) return FA_ERR_BAD_ARG;
+  if (B > 0 && (!seq_lens_host || !splits_out)) return FA_ERR_NULL_PTR;
+  const int S = fa::decode_max_splits(B, Hkv, max_pages_per_seq, window, num_splits);
+  const int C = fa::decode_chunk_tokens(B, Hkv);
+  const long long max_len = static_cast<long long>(max_pages_per_seq) * FA_PAGE_SIZE;
+  for (int b = 0; b < B; ++b)
+    splits_out[b] =
+        fa::decode_splits(fa::visible_tokens(seq_lens_host[b], window, max_len), C, S, num_splits);
+  return FA_OK;
 }
 
 }  // extern "C"
@@ -261,11 +271,10 @@ namespace {
 // then lse [B, H, S] fp32 at the next 256-byte boundary.
 void set_partials(fa::DecodeArgs* a, void* workspace) {
   const size_t rows = static_cast<size_t>(a->B) * a->H * a->max_splits;
-  a->part_o = static_cast<float*>(workspace);
-  a->part_lse = workspace ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                                     (rows * a->d * sizeof(float) + 255) / 256 *
-                                                         256)
-                          : nullptr;
+  char* w = static_cast<char*>(workspace);
+  a->part_o = reinterpret_cast<float*>(w);
+  a->part_lse =
+      w ? reinterpret_cast<float*>(w + (rows * a->d * sizeof(float) + 255) / 256 * 256) : nullptr;
 }
 
 // Validates a decode call and fills `a`; launches nothing. `*empty` is set
@@ -292,7 +301,10 @@ fa_status decode_prepare(const void* q, const void* K_pool, const void* V_pool,
   if (int64_t{num_pages} * page_size * Hkv * d > kMaxElems ||
       int64_t{B} * max_pages_per_seq > kMaxElems || int64_t{B} * H * d > kMaxElems ||
       int64_t{max_pages_per_seq} * page_size > kMaxElems || B > 65535 || Hkv > 65535 ||
-      !merge_fits(int64_t{B} * H))
+      !merge_fits(int64_t{B} * H) ||
+      !grid_fits(int64_t{B} * Hkv *
+                     fa::decode_max_splits(B, Hkv, max_pages_per_seq, window, num_splits),
+                 kDecodeThreads))
     return FA_ERR_BAD_SHAPE;
   if (B == 0) {
     *empty = true;
@@ -301,8 +313,9 @@ fa_status decode_prepare(const void* q, const void* K_pool, const void* V_pool,
   if (!q || !K_pool || !V_pool || !block_table || !seq_lens || !O || !LSE)
     return FA_ERR_NULL_PTR;
   if (!aligned16(q) || !aligned16(K_pool) || !aligned16(V_pool)) return FA_ERR_BAD_ARG;
-  const int S = fa::decode_max_splits(B, Hkv, num_splits);
-  const size_t need = fa_decode_workspace_size(B, H, Hkv, d, num_splits);
+  const int S = fa::decode_max_splits(B, Hkv, max_pages_per_seq, window, num_splits);
+  const size_t need =
+      fa_decode_workspace_size(B, H, Hkv, d, max_pages_per_seq, window, num_splits);
   if (check_workspace && S > 1 && (workspace == nullptr || workspace_bytes < need))
     return FA_ERR_WORKSPACE;
   fa::DecodeArgs a;
@@ -377,7 +390,8 @@ fa_status fa_decode_paged_noalloc(const void* q, const void* K_pool, const void*
                                 window, softcap, dtype, out_dtype, nullptr, 0, &a, &empty,
                                 /*check_workspace=*/false);
   if (st != FA_OK || empty) return st;
-  if (fa_decode_workspace_size(B, H, Hkv, d, num_splits) > fa::kDecodeScratchBytes)
+  if (fa_decode_workspace_size(B, H, Hkv, d, max_pages_per_seq, window, num_splits) >
+      fa::kDecodeScratchBytes)
     return FA_ERR_SCRATCH;
   void* ws = nullptr;
   if (fa::decode_scratch(&ws) != hipSuccess) return FA_ERR_HIP;

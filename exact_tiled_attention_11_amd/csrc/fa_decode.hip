@@ -77,6 +77,7 @@ __device__ __forceinline__ int first_visible(int len, int window) {
   return (window > 0 && len > window) ? len - window : 0;
 }
 
+
 __device__ __forceinline__ float nanf_() { return __builtin_nanf(""); }
 
 // K rows in the ring have their 16-byte chunks permuted by an XOR with
@@ -153,12 +154,25 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecParams a) 
   __shared__ float wm[kDecWaves][GP], wl[kDecWaves][GP];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+  // Workgroups u = S q + slot serve (sequence, KV head) pair q = b Hkv + hk,
+  // the pairs in order; slot holds chunk (slot - q) mod S, so that the active
+  // chunks 0 .. nsplit-1 of consecutive pairs start on consecutive XCDs (the
+  // dispatcher sends workgroup u to XCD u % 8) and spread over all of them
+  // whatever the sequences' chunk counts. Workgroups past a sequence's last
+  // chunk leave at once.
+  const int S = a.max_splits;
+  const int u = static_cast<int>(blockIdx.x);
+  const int pq = u / S, slot = u - pq * S;
+  int split = slot - pq % S;
+  if (split < 0) split += S;
+  const int b = pq / a.Hkv, hk = pq - b * a.Hkv;
   const int G = a.group;
+  const long long max_len = static_cast<long long>(a.max_pages) * kPage;
   const int len = a.seq_lens[b];
-  const bool bad_len = len < 0 || len > a.max_pages * kPage;
+  const bool bad_len = len < 0 || len > max_len;
   const int kv_start = bad_len ? 0 : first_visible(len, a.window);
-  const int nsplit = decode_splits(bad_len ? 0 : len - kv_start, a.max_splits, a.num_splits);
+  const int nsplit = decode_splits(visible_tokens(len, a.window, max_len),
+                                   decode_chunk_tokens(a.B, a.Hkv), a.max_splits, a.num_splits);
   if (split >= nsplit) return;                 // whole workgroup: uniform
   const int npages = bad_len ? 0 : (len + kPage - 1) / kPage;
   const int p0 = kv_start / kPage;             // first page holding a visible key
@@ -371,13 +385,15 @@ struct MergeParams {
   const float* o_parts;
   const float* lse_parts;
   const int32_t* num_parts;   // per row, or NULL
-  const int32_t* seq_lens;    // decode mode: parts per row from the split rule
+  const int32_t* seq_lens;    // decode mode: parts per row from the split plan
   void* o;
   float* lse;
   int R, S, d;
   int heads;                  // decode mode: rows per sequence
-  int fixed_splits;           // decode mode: num_splits argument (0: the rule, capped at S)
-  int max_len;                // decode mode: max_pages * page_size
+  int Hkv;                    // decode mode: KV heads per sequence
+  int B;                      // decode mode: sequences
+  int fixed_splits;           // decode mode: num_splits argument
+  long long max_len;          // decode mode: max_pages * page_size
   int window;                 // decode mode: visible-key window (0 = all)
   const float* o_extra;       // optional part S of every row: [R, d] ...
   const float* lse_extra;     // ... and [R] (NULL: none)
@@ -393,9 +409,8 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams a) {
   if (r >= a.R) return;
   int n;
   if (DECODE) {
-    const int len = a.seq_lens[r / a.heads];
-    const bool bad = len < 0 || len > a.max_len;
-    n = decode_splits(bad ? 0 : len - first_visible(len, a.window), a.S, a.fixed_splits);
+    n = decode_splits(visible_tokens(a.seq_lens[r / a.heads], a.window, a.max_len),
+                      decode_chunk_tokens(a.B, a.Hkv), a.S, a.fixed_splits);
     if (n <= 1) return;   // written directly by the decode kernel
   } else {
     n = a.num_parts ? a.num_parts[r] : a.S;
@@ -549,7 +564,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   p.cap_over_scale = a.softcap > 0.f ? a.softcap / a.scale : 0.f;
   p.scale_over_cap = a.softcap > 0.f ? a.scale / a.softcap : 0.f;
   const int G = a.H / a.Hkv;
-  const dim3 grid(a.max_splits, a.Hkv, a.B);
+  const dim3 grid(static_cast<unsigned>(a.max_splits * a.B * a.Hkv));
   hipError_t e;
   if (a.dtype == FA_BF16)
     e = a.out_dtype == FA_F32 ? launch_decode_d<BF16, float>(p, a.d, G, grid, s)
@@ -570,8 +585,10 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   m.S = a.max_splits;
   m.d = a.d;
   m.heads = a.H;
+  m.Hkv = a.Hkv;
+  m.B = a.B;
   m.fixed_splits = a.num_splits;
-  m.max_len = a.max_pages * kPage;
+  m.max_len = static_cast<long long>(a.max_pages) * kPage;
   m.window = a.window;
   m.o_extra = nullptr;
   m.lse_extra = nullptr;
@@ -590,6 +607,8 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
   m.S = a.S;
   m.d = a.d;
   m.heads = 1;
+  m.Hkv = 1;
+  m.B = 0;
   m.fixed_splits = 0;
   m.max_len = 0;
   m.window = 0;

@@ -216,33 +216,41 @@ fa_status fa_cascade(const void* Q, const int32_t* qo_indptr,
  * to fill the GPU, the count chosen from the batch size, the head count and
  * the context length).
  *
- * fa_decode_max_splits - the most chunks any sequence of a batch of B
- * sequences with Hkv KV heads is cut into, which is also the number of
- * partial slots per (sequence, head) in the workspace. num_splits > 0 forces
- * that count; num_splits == 0 gives ceil(8192 / (B * Hkv)) clamped to
- * [1, FA_MAX_SPLITS]: about 8192 (sequence, KV head, chunk) workgroups in all
- * when every sequence is long (64 at batch 1 with 8 KV heads, 16 at 64
- * sequences, 4 at 256). Returns -1 for invalid input.
+ * With num_splits == 0 a sequence with v visible tokens (min(seq_lens[b],
+ * window) with a window, else seq_lens[b]) is cut into min(ceil(v / C), K)
+ * chunks, with P = B * Hkv (sequence, KV head) pairs,
+ * C = clamp(4 * P, 1024, 4096) tokens and K = ceil(4096 / P): short chunks
+ * when few pairs have to fill the GPU (one 32K-token sequence over 8 KV heads:
+ * 32 chunks per head, 256 workgroups), long and few when the pairs already do
+ * (64 sequences x 8 KV heads: chunks of 2048 tokens, at most 8). num_splits > 0
+ * forces that count for every sequence. Chunks are near-equal and
+ * page-aligned; the kernels evaluate the rule on the device from seq_lens.
  *
- * fa_decode_num_splits - the number of key chunks a sequence with seq_len
- * visible tokens gets in that batch: num_splits > 0 forces it; num_splits ==
- * 0 gives ceil(seq_len / 256) clamped to [1, fa_decode_max_splits(B, Hkv, 0)],
- * so no chunk is shorter than 256 tokens unless the sequence is. Chunks are
- * near-equal and page-aligned. Returns -1 for invalid input (B, Hkv >= 1).
+ * fa_decode_max_splits - partial slots per (sequence, head) in the
+ * workspace: num_splits if > 0, else min(ceil(L / C), K) clamped to
+ * [1, FA_MAX_SPLITS] with L = max_pages_per_seq * FA_PAGE_SIZE (or window if
+ * window > 0 and smaller). Returns -1 for invalid input.
  *
- * Pure host functions; the kernels evaluate the same rule on the device.
+ * fa_decode_plan - the same plan on the host for a host copy of the lengths:
+ * writes each sequence's chunk count to splits_out[B]. For inspection and
+ * tests; the decode call does not need it.
  */
-int fa_decode_max_splits(int B, int Hkv, int num_splits);
-int fa_decode_num_splits(int seq_len, int B, int Hkv, int num_splits);
+int fa_decode_max_splits(int B, int Hkv, int max_pages_per_seq, int window,
+                         int num_splits);
+fa_status fa_decode_plan(const int32_t* seq_lens_host, int B, int Hkv,
+                         int max_pages_per_seq, int window, int num_splits,
+                         int32_t* splits_out);
 
 /*
- * fa_decode_workspace_size - bytes of device workspace fa_decode_paged needs
- * for B sequences of H query heads (Hkv KV heads) of dimension d and the
- * given num_splits (0 = automatic): one fp32 partial (o[d], lse) per
- * (b, h, slot), fa_decode_max_splits(B, Hkv, num_splits) slots each.
- * Returns 0 for invalid sizes.
+ * fa_decode_workspace_size - bytes of device workspace fa_decode_paged (and
+ * fa_decode_paged_ex with the same window) needs for B sequences of H query
+ * heads (Hkv KV heads) of dimension d: one fp32 partial (o[d], lse) per
+ * (b, h, slot), fa_decode_max_splits(B, Hkv, max_pages_per_seq, window,
+ * num_splits) slots each. Returns 0 for invalid sizes.
  */
-size_t fa_decode_workspace_size(int B, int H, int Hkv, int d, int num_splits);
+size_t fa_decode_workspace_size(int B, int H, int Hkv, int d,
+                                int max_pages_per_seq, int window,
+                                int num_splits);
 
 /*
  * fa_decode_paged - one query token per sequence against a paged KV cache.
@@ -269,9 +277,10 @@ size_t fa_decode_workspace_size(int B, int H, int Hkv, int d, int num_splits);
  *   seq_lens     [B]                     int32      device memory
  *   O            [B, H, d]                          out_dtype (dtype or FA_F32)
  *   LSE          [B, H]                  float
- *   workspace    >= fa_decode_workspace_size(B, H, Hkv, d, num_splits) bytes
- *                of device memory (may be NULL when that count of slots is
- *                1); contents on entry are ignored, on exit unspecified.
+ *   workspace    >= fa_decode_workspace_size(B, H, Hkv, d, max_pages_per_seq,
+ *                0, num_splits) bytes of device memory (may be NULL when the
+ *                slot count is 1); contents on entry are ignored, on exit
+ *                unspecified.
  *
  * Supported: dtype in {FA_F16, FA_BF16}; d in {64, 128}; page_size ==
  * FA_PAGE_SIZE; 0 <= num_splits <= FA_MAX_SPLITS; H % Hkv == 0 and
@@ -305,9 +314,9 @@ fa_status fa_decode_paged(const void* q, const void* K_pool,
  *   softcap > 0  each scaled score x = scale * q.k is replaced by
  *                softcap * tanh(x / softcap) before the softmax; LSE is the
  *                log-sum-exp of the capped scores. softcap == 0 disables it.
- * The chunk count of a sequence is fa_decode_num_splits(v, B, Hkv, num_splits)
- * with v = the number of visible tokens (min(seq_lens[b], window) for
- * window > 0).
+ * The split plan counts visible tokens only (min(seq_lens[b], window) for
+ * window > 0), and the workspace is fa_decode_workspace_size(B, H, Hkv, d,
+ * max_pages_per_seq, window, num_splits) bytes.
  * Everything else (layouts, workspace, support, contract, NaN on contract
  * violation) is as for fa_decode_paged; window < 0 or a negative or
  * non-finite softcap returns FA_ERR_BAD_ARG. With window == 0 and
@@ -336,9 +345,10 @@ fa_status fa_decode_paged_ex(const void* q, const void* K_pool,
  * nothing. Every partial the merge reads is written by the same call first,
  * so nothing needs clearing between calls.
  *
- * Limit: fa_decode_workspace_size(B, H, Hkv, d, num_splits) must not exceed
- * FA_NOALLOC_SCRATCH_BYTES, else FA_ERR_SCRATCH (nothing launched). The
- * 64-sequence, 32/8-head, d = 128 batch with automatic splits needs 16.8 MB.
+ * Limit: fa_decode_workspace_size(B, H, Hkv, d, max_pages_per_seq, window,
+ * num_splits) must not exceed FA_NOALLOC_SCRATCH_BYTES, else FA_ERR_SCRATCH
+ * (nothing launched). The 64-sequence, 32/8-head, d = 128 batch of up to
+ * 32768 tokens per sequence with automatic splits needs 8.5 MB.
  *
  * Runs on the current HIP device. All calls on one device share its buffer:
  * calls that overlap in time on one device (different streams, threads, or

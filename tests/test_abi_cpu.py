@@ -127,9 +127,10 @@ def test_decode_ex_validation(kw, status):
 
 def test_decode_ex_workspace_checks():
     p = [FAKE] * 7
-    need = fa.decode_workspace_size(2, 8, 2, 128, 0)
-    assert dec_ex(window=100, ptrs=p, ws=None, ws_bytes=need) == WS
-    assert dec_ex(window=100, ptrs=p, ws=FAKE, ws_bytes=need - 1) == WS
+    need = fa.decode_workspace_size(2, 8, 2, 128, 200, 2000, 0)
+    assert fa.decode_max_splits(2, 2, 200, 2000) == 2
+    assert dec_ex(window=2000, max_pages=200, ptrs=p, ws=None, ws_bytes=need) == WS
+    assert dec_ex(window=2000, max_pages=200, ptrs=p, ws=FAKE, ws_bytes=need - 1) == WS
 
 
 def test_decode_graph_validation_before_any_hip_call():
@@ -138,7 +139,7 @@ def test_decode_graph_validation_before_any_hip_call():
     h = ctypes.c_void_p()
 
     def create(out, window=0, softcap=0.0, splits=0, ptrs=p, B=2, ws=None, ws_bytes=0):
-        return lib.fa_decode_graph_create(out, *ptrs, B, 8, 2, 128, 16, 4, 8, 0.1, splits,
+        return lib.fa_decode_graph_create(out, *ptrs, B, 8, 2, 128, 16, 200, 8, 0.1, splits,
                                           window, softcap, BF16, BF16, ws, ws_bytes)
     assert create(None) == NULL
     assert create(ctypes.byref(h), window=-1) == ARG
@@ -235,41 +236,73 @@ def test_cascade_pointer_and_workspace_checks():
 
 def test_decode_workspace_checks():
     p = [FAKE] * 7
-    need = fa.decode_workspace_size(2, 8, 2, 128, 0)
+    # B = 2, Hkv = 2: chunks of 1024 tokens. 4 pages of 16 tokens: one chunk at
+    # most, no workspace needed; 200 pages: ceil(3200 / 1024) = 4 slots
+    assert fa.decode_max_splits(2, 2, 4) == 1 and fa.decode_max_splits(2, 2, 200) == 4
+    need = fa.decode_workspace_size(2, 8, 2, 128, 200, 0, 0)
     assert need > 0
-    assert dec(ptrs=p, ws=None, ws_bytes=need) == WS
-    assert dec(ptrs=p, ws=FAKE, ws_bytes=need - 1) == WS
-    need4 = fa.decode_workspace_size(2, 8, 2, 128, 4)
-    assert need4 < need
+    assert dec(max_pages=200, ptrs=p, ws=None, ws_bytes=need) == WS
+    assert dec(max_pages=200, ptrs=p, ws=FAKE, ws_bytes=need - 1) == WS
+    need4 = fa.decode_workspace_size(2, 8, 2, 128, 4, 0, 4)
     assert dec(ptrs=p, splits=4, ws=FAKE, ws_bytes=need4 - 4) == WS
 
 
-def test_split_rule_and_workspace_size():
-    # the cap: ceil(8192 / (B * Hkv)) clamped to [1, 64]
-    assert [fa.decode_max_splits(B, 8) for B in (1, 2, 4, 8, 16, 32, 64, 128, 256, 1024, 2048)] \
-        == [64, 64, 64, 64, 64, 32, 16, 8, 4, 1, 1]
-    assert fa.decode_max_splits(3, 5) == 64 and fa.decode_max_splits(100, 1) == 64
-    assert fa.decode_max_splits(100, 2) == 41 and fa.decode_max_splits(0, 8) == 64
-    assert [fa.decode_max_splits(64, 8, s) for s in (1, 7, 64)] == [1, 7, 64]
-    assert fa.decode_max_splits(1, 0) == -1 and fa.decode_max_splits(1, 8, 65) == -1
-    # per sequence: ceil(len / 256) under the cap
-    lens = (0, 1, 256, 257, 1024, 2049, 3840, 4096, 4097, 16384, 16385, 10**6)
-    assert [fa.decode_num_splits(n, 64, 8) for n in lens] == \
-        [1, 1, 1, 2, 4, 9, 15, 16, 16, 16, 16, 16]
-    assert [fa.decode_num_splits(n, 1, 8) for n in lens] == \
-        [1, 1, 1, 2, 4, 9, 15, 16, 17, 64, 64, 64]
-    assert fa.decode_num_splits(32768, 1, 8) == 64 and fa.decode_num_splits(32768, 256, 8) == 4
-    assert [fa.decode_num_splits(100, 64, 8, s) for s in range(1, 65)] == list(range(1, 65))
-    assert fa.decode_num_splits(-1, 1, 1) == -1 and fa.decode_num_splits(5, 1, 1, 65) == -1
-    assert fa.decode_num_splits(5, 0, 1) == -1
-    # fp32 o-partials, 256-byte aligned, followed by the fp32 lse-partials
-    assert fa.decode_workspace_size(64, 32, 8, 128, 0) == \
-        64 * 32 * 16 * 128 * 4 + 64 * 32 * 16 * 4
-    assert fa.decode_workspace_size(1, 32, 8, 128, 0) == 32 * 64 * 128 * 4 + 32 * 64 * 4
-    assert fa.decode_workspace_size(1, 1, 1, 1, 1) == 256 + 4
-    assert fa.decode_workspace_size(1, 1, 1, 1, -1) == 0
-    assert fa.decode_workspace_size(1, 1, 1, 1, 65) == 0
-    assert fa.decode_workspace_size(1, 3, 2, 1, 0) == 0
+def plan_by_hand(lens, Hkv, max_pages, window=0, fixed=0):
+    """The split plan written out from its definition."""
+    L = max_pages * 16
+    vis = [0 if (x < 0 or x > L) else (min(x, window) if window > 0 else x) for x in lens]
+    P = max(1, len(lens)) * Hkv
+    C = min(4096, max(1024, 4 * P))
+    Lv = min(L, window) if window > 0 else L
+    S = fixed if fixed > 0 else min(64, max(1, min(-(-Lv // C), -(-4096 // P))))
+    if fixed > 0:
+        return [fixed] * len(lens), S
+    return [min(S, max(1, -(-v // C))) for v in vis], S
+
+
+def test_split_plan_and_workspace_size():
+    from exact_tiled_attention_11_amd import inputs
+    # slots: min(ceil(L / C), ceil(4096 / P)), C = clamp(4 P, 1024, 4096), P = B Hkv
+    assert [fa.decode_max_splits(1, 8, mp) for mp in (1, 64, 65, 2048, 4096, 8192)] == \
+        [1, 1, 2, 32, 64, 64]
+    assert [fa.decode_max_splits(B, 8, 2048) for B in (1, 8, 16, 24, 32, 64, 128, 256)] == \
+        [32, 32, 32, 22, 16, 8, 4, 2]
+    assert fa.decode_max_splits(64, 8, 2048, 4096) == 2
+    assert fa.decode_max_splits(1, 8, 2048, 4096) == 4
+    assert fa.decode_max_splits(1, 8, 2048, 100) == 1
+    assert fa.decode_max_splits(64, 8, 2048, 0, 7) == 7
+    assert fa.decode_max_splits(1, 8, 0) == -1 and fa.decode_max_splits(1, 8, 8, -1) == -1
+    assert fa.decode_max_splits(1, 8, 8, 0, 65) == -1 and fa.decode_max_splits(1, 0, 8) == -1
+    # one sequence of 32K tokens over 8 KV heads: chunks of 1024 tokens, 256 workgroups
+    assert list(fa.decode_plan([32768], 8, 2048)) == [32]
+    assert list(fa.decode_plan([32768], 1, 2048)) == [32]
+    assert list(fa.decode_plan([32768] * 8, 8, 2048)) == [32] * 8
+    assert list(fa.decode_plan([1000, 0, 1], 8, 2048)) == [1, 1, 1]
+    # the 64-sequence workload: chunks of 2048 tokens, at most 8 per sequence
+    lens = [int(x) for x in inputs.uniform_lengths(64, 1024, 32768, 104)]
+    got = fa.decode_plan(lens, 8, 2048)
+    want, S = plan_by_hand(lens, 8, 2048)
+    assert list(got) == want and S == 8
+    assert list(got) == [min(8, -(-x // 2048)) for x in lens]
+    # with a 4096-token window: two chunks for every sequence that long
+    got = fa.decode_plan(lens, 8, 2048, window=4096)
+    assert list(got) == plan_by_hand(lens, 8, 2048, 4096)[0]
+    assert list(got) == [min(2, -(-x // 2048)) for x in lens]
+    # fixed counts, lengths outside the table (visible 0)
+    assert list(fa.decode_plan(lens[:3], 8, 2048, 0, 5)) == [5, 5, 5]
+    assert list(fa.decode_plan([-1, 10 ** 6, 5000], 2, 2048)) == [1, 1, 5]
+    assert list(fa.decode_plan([], 8, 2048)) == []
+    with pytest.raises(fa.FAError):
+        fa.decode_plan([1], 0, 2048)
+    # fp32 o-partials, then fp32 lse-partials at a 256-byte boundary
+    assert fa.decode_workspace_size(64, 32, 8, 128, 2048) == \
+        64 * 32 * 8 * 128 * 4 + 64 * 32 * 8 * 4
+    assert fa.decode_workspace_size(1, 32, 8, 128, 2048) == 32 * 32 * 128 * 4 + 32 * 32 * 4
+    assert fa.decode_workspace_size(1, 1, 1, 1, 1, 0, 1) == 256 + 4
+    assert fa.decode_workspace_size(1, 1, 1, 1, 1, 0, -1) == 0
+    assert fa.decode_workspace_size(1, 1, 1, 1, 1, 0, 65) == 0
+    assert fa.decode_workspace_size(1, 1, 1, 1, 0, 0, 0) == 0
+    assert fa.decode_workspace_size(1, 3, 2, 1, 1, 0, 0) == 0
 
 
 @pytest.mark.parametrize("args,status", [
@@ -329,6 +362,7 @@ def test_decode_noalloc_validation(kw, status):
 
 def test_decode_noalloc_rejects_more_partials_than_its_scratch():
     p = [FAKE] * 7
-    # 64 sequences of 128 query heads over 8 KV heads need 67 MB of partials
-    assert fa.decode_workspace_size(64, 128, 8, 128, 0) > 32 << 20
-    assert dec_noalloc(B=64, H=128, Hkv=8, max_pages=2048, num_pages=1 << 16, ptrs=p) == SCRATCH
+    # 64 sequences of 128 query heads, 64 fixed splits: 270 MB of partials
+    assert fa.decode_workspace_size(64, 128, 8, 128, 2048, 0, 64) > 32 << 20
+    assert dec_noalloc(B=64, H=128, Hkv=8, max_pages=2048, num_pages=1 << 16, splits=64,
+                       ptrs=p) == SCRATCH

@@ -169,11 +169,11 @@ def test_paged_decode_b64_h32_kv8(c4, splits):
 def test_paged_decode_batch1_32k_worked_example(splits):
     """The pages' occupancy example ("3.4 Attention Kernels", "Worked example"):
     one sequence of 32768 tokens, 32 query heads over 8 KV heads, d = 128. The
-    automatic plan cuts it into 64 chunks (512 workgroups), the fixed 16 is the
-    page's own count."""
+    automatic plan cuts it into 32 chunks (256 workgroups), the fixed 16 is the
+    page's own count, 64 the most the library allows."""
     lens = [32768]
     pi = inputs.paged_decode_inputs(1, 32, 8, 128, lens, seed=141)
-    assert fa.decode_num_splits(32768, 1, 8) == 64
+    assert list(fa.decode_plan([32768], 8, pi.block_table.shape[1])) == [32]
     say(f"decode batch 1, 32k tokens, splits={splits}: oracle")
     ro, rl = oracle.decode_paged(pi.q, pi.k_pool, pi.v_pool, pi.block_table, pi.seq_lens,
                                  1 / math.sqrt(128))

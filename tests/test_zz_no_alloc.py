@@ -83,9 +83,9 @@ def test_noalloc_equals_workspace_decode_twice_shrinking(out_dtype):
 
 
 def test_noalloc_paged_decode_workload_and_limit():
-    """The 64-sequence, 32/8-head workload fits the buffer (16.8 MB of
-    partials); a batch whose partials would not fit is refused before any
-    launch, with the outputs untouched."""
+    """The 64-sequence, 32/8-head workload fits the buffer (8.5 MB of
+    partials); a batch whose partials would not fit (64 fixed splits of 128
+    query heads) is refused before any launch, with the outputs untouched."""
     p = inputs.WORKLOADS["paged_decode_bf16_b64_h32_kv8"].params
     lens = inputs.uniform_lengths(p["B"], p["len_lo"], p["len_hi"], p["seed"])
     pi = inputs.paged_decode_inputs(p["B"], p["H"], p["Hkv"], p["d"], lens, p["seed"],
@@ -94,17 +94,16 @@ def test_noalloc_paged_decode_workload_and_limit():
     d = to_dev(pi)
     (eo, el), (no, nl) = call_both(d, 0, 0.0, 0, torch.bfloat16)
     assert torch.equal(no, eo) and torch.equal(nl, el)
-    # 128 query heads over 8 KV heads at 64 sequences: 67 MB of partials
+    # 128 query heads over 8 KV heads at 64 sequences, 64 chunks each: 270 MB
     B, H, Hkv = 64, 128, 8
-    assert fa.decode_workspace_size(B, H, Hkv, 128, 0) > fa.lib().fa_decode_workspace_size(
-        64, 32, 8, 128, 0) * 3
+    assert fa.decode_workspace_size(B, H, Hkv, 128, d["t"].shape[1], 0, 64) > 32 << 20
     q = torch.zeros((B, H, 128), dtype=torch.bfloat16, device=DEV)
     out = torch.full((B, H, 128), 7.0, dtype=torch.bfloat16, device=DEV)
     lse = torch.full((B, H), 7.0, dtype=torch.float32, device=DEV)
     st = fa.lib().fa_decode_paged_noalloc(
         q.data_ptr(), d["k"].data_ptr(), d["v"].data_ptr(), d["t"].data_ptr(), d["s"].data_ptr(),
         out.data_ptr(), lse.data_ptr(), B, H, Hkv, 128, 16, d["t"].shape[1], d["k"].shape[0],
-        1 / math.sqrt(128), 0, 0, 0.0, BF16, BF16,
+        1 / math.sqrt(128), 64, 0, 0.0, BF16, BF16,
         ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
     torch.cuda.synchronize()
     assert st == 7, fa.status_string(st)
