@@ -169,61 +169,37 @@ struct TileLoader {
 };
 
 // The same share of a K or V tile when the keys live in 16-token pages: key
-// k0 + row is slot row % 16 of page ids[row / 16] (a 64-key tile spans four
-// pages). Every slab lies inside one page.
+// k0 + row is slot row % 16 of the tile's page row / 16 (a 64-key tile spans
+// four pages). A wave's slabs cover kBC / NW consecutive rows, all inside one
+// page (page WAVE_ROWS * wave / 16 of the tile), so one page id per wave and
+// tile addresses them.
 constexpr int kPageTokens = FA_PAGE_SIZE;
-
-__device__ __forceinline__ int pick_id(int4 ids, int i) {
-  return i == 0 ? ids.x : i == 1 ? ids.y : i == 2 ? ids.z : ids.w;
-}
 
 template <int D, int NW>
 struct PagedTileLoader {
   static constexpr int CPR = D / 8;
   static constexpr int RPS = 64 / CPR;                 // key rows per slab
   static constexpr int SPW = kBC * CPR / 64 / NW;
-  static_assert(kPageTokens % RPS == 0, "a slab must not straddle pages");
+  static constexpr int WAVE_ROWS = SPW * RPS;
+  static_assert(WAVE_ROWS * NW == kBC && kPageTokens % WAVE_ROWS == 0,
+                "a wave's slabs must lie in one page");
   uint32_t voff[SPW];   // byte offset of this lane's chunk from the start of its page
-  int coff[SPW];        // swizzled chunk offset alone (elements)
-  int row[SPW];
-  int pidx[SPW];        // which of the tile's four pages slab r lies in (wave-uniform)
-  uint32_t lds0;
+  uint32_t lds0;        // byte offset of this wave's first slab in a tile (wave-uniform)
 
   __device__ __forceinline__ PagedTileLoader(int64_t rs, int wave, int lane) {
     const int slab0 = wave * SPW;
 #pragma unroll
     for (int r = 0; r < SPW; ++r) {
       const int slot = (slab0 + r) * 64 + lane;
-      row[r] = slot / CPR;
-      coff[r] = ((slot % CPR) ^ swz<D>(row[r])) * 8;
-      voff[r] = static_cast<uint32_t>(((row[r] % kPageTokens) * rs + coff[r]) * 2);
-      pidx[r] = __builtin_amdgcn_readfirstlane((slab0 + r) * RPS / kPageTokens);
+      const int row = slot / CPR;
+      const int coff = ((slot % CPR) ^ swz<D>(row)) * 8;
+      voff[r] = static_cast<uint32_t>(((row % kPageTokens) * rs + coff) * 2);
     }
     lds0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(slab0 * 1024));
   }
-
-  // Copies of this wave's slabs of the tile at key k0, whose four page ids
-  // are `ids`, into the tile at LDS byte address `lds`. A slab lies in one
-  // page, so its base is wave-uniform. Rows past the last key re-read the
-  // last key, as in TileLoader (the ragged last tile, with per-lane pages).
-  __device__ __forceinline__ void load(const uint16_t* base, int64_t rs, int k0, int nk,
-                                       int4 ids, uint32_t lds) const {
-    const int64_t pstride = rs * kPageTokens;
-    if (__builtin_expect(k0 + kBC > nk, 0)) {
-#pragma unroll
-      for (int r = 0; r < SPW; ++r) {
-        const int key = min(k0 + row[r], nk - 1);
-        const int id = pick_id(ids, key / kPageTokens - k0 / kPageTokens);
-        load_lds16_async(base + static_cast<int64_t>(id) * pstride + (key % kPageTokens) * rs +
-                             coff[r],
-                         lds + lds0 + r * 1024);
-      }
-    } else {
-#pragma unroll
-      for (int r = 0; r < SPW; ++r)
-        load_lds16_sbase(base + static_cast<int64_t>(pick_id(ids, pidx[r])) * pstride, voff[r],
-                         lds + lds0 + r * 1024);
-    }
+  // Which of a tile's four pages holds this wave's rows.
+  static __device__ __forceinline__ int page_of_wave(int wave) {
+    return wave * WAVE_ROWS / kPageTokens;
   }
 };
 
@@ -346,31 +322,32 @@ void fwd16_kernel(const FwdParams a) {
     kbase += static_cast<int64_t>(b) * a.Nk * kv_rs;
     vbase += static_cast<int64_t>(b) * a.Nk * kv_rs;
   }
-  // Paged: page ids of a tile are fetched one step before they are needed and
-  // made wave-uniform only at the top of the step that uses them, when no
-  // K/V copy is in flight (so the wait for them never holds copies back).
-  // Ids past the sequence's last page are never used (rows past the last key
-  // re-read that key); an id outside the pool is replaced by page 0 and marks
-  // the sequence bad.
+  // Paged: a wave's share of a 64-key tile lies in one 16-token page (page
+  // wave / 2 of the tile's four), so each copy needs one page id per wave,
+  // read from the block table by a scalar load one step before the copy is
+  // issued. A page past the sequence's last one is never read (its resource
+  // covers no rows); an id outside the pool is replaced by page 0 and marks
+  // the sequence bad (NaN output, agreed over all waves at the end).
   const int32_t* table = PAGED ? a.block_table + static_cast<int64_t>(b) * a.max_pages : nullptr;
   const int last_page = Nk > 0 ? (Nk - 1) / kPageTokens : 0;
+  const int wave_page = PagedTileLoader<D, NW>::page_of_wave(wave);
   bool bad_page = false;
-  auto fetch_ids = [&](int t) {
-    return make_int4(table[min(t * 4, last_page)], table[min(t * 4 + 1, last_page)],
-                     table[min(t * 4 + 2, last_page)], table[min(t * 4 + 3, last_page)]);
-  };
-  auto use_ids = [&](int4 raw) {
-    int v[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int id = __builtin_amdgcn_readfirstlane(v[i]);
-      if (id < 0 || id >= a.num_pages) {
-        bad_page = true;
-        id = 0;
-      }
-      v[i] = id;
+  // The id as loaded (a vector register, the same in every lane); made
+  // wave-uniform only where it is used, a step later, so that the load's
+  // latency hides behind that step instead of stalling this one.
+  auto fetch_id = [&](int t) { return table[min(t * 4 + wave_page, last_page)]; };
+  auto load_id = [&](int t) { return __builtin_amdgcn_readfirstlane(fetch_id(t)); };
+  // Buffer resource over the rows of this wave's page of key tile t that
+  // hold keys (none past the sequence's last key: those copy as zeros).
+  auto page_rsrc = [&](const uint16_t* base, int id, int t) {
+    if (id < 0 || id >= a.num_pages) {
+      bad_page = true;
+      id = 0;
     }
-    return make_int4(v[0], v[1], v[2], v[3]);
+    const int first = t * kBC + wave_page * kPageTokens;
+    const int valid = min(max(Nk - first, 0), kPageTokens);
+    return buffer_rsrc(base + static_cast<int64_t>(id) * kv_rs * kPageTokens,
+                       valid > 0 ? static_cast<uint32_t>((valid - 1) * kv_rs32 + D) * 2u : 0u);
   };
 
   // Per-lane LDS read addresses (bytes, LDS address space) in the first K
@@ -405,34 +382,35 @@ void fwd16_kernel(const FwdParams a) {
 
   const TileLoader<D, NW> loader(kv_rs, wave, lane);
   const PagedTileLoader<D, NW> ploader(kv_rs, wave, lane);
-  // Paged: validated ids of the tile whose V is copied next (= the K tile of
-  // the previous step) and fetched ids of the K tile of the next step.
-  int4 ids_v = make_int4(0, 0, 0, 0), ids_next = make_int4(0, 0, 0, 0);
-  auto copy_k = [&](int g, int4 ids, uint32_t dst) {
-    if constexpr (PAGED)
-      ploader.load(kbase, kv_rs, tile_at(g) * kBC, Nk, ids, dst);
-    else
-      loader.load(kbase, kv_rs, tile_at(g) * kBC, Nk, dst);
-  };
-  auto copy_v = [&](int g, int4 ids, uint32_t dst) {
-    if constexpr (PAGED)
-      ploader.load(vbase, kv_rs, tile_at(g) * kBC, Nk, ids, dst);
-    else
-      loader.load(vbase, kv_rs, tile_at(g) * kBC, Nk, dst);
+  // Paged: page id of the tile whose V is copied next (= the K tile of the
+  // previous step) and, as fetched, of the K tile copied next.
+  int id_v = 0, raw_k = 0;
+  auto copy_k = [&](int g, uint32_t dst) { loader.load(kbase, kv_rs, tile_at(g) * kBC, Nk, dst); };
+  auto copy_v = [&](int g, uint32_t dst) { loader.load(vbase, kv_rs, tile_at(g) * kBC, Nk, dst); };
+  // This wave's slabs of a paged tile, from a page resource.
+  auto copy_paged = [&](i32x4 rsrc, uint32_t dst) {
+#pragma unroll
+    for (int r = 0; r < PagedTileLoader<D, NW>::SPW; ++r)
+      load_lds16_buf(rsrc, ploader.voff[r], dst + ploader.lds0 + r * 1024);
   };
   // First copies of a segment whose first step is g: K and V of step g into
   // slot 0, K of step g + 1 into K slot 1 (when the segment has it).
   auto segment_copies = [&](int g, int nt) {
     if (nt <= 0) return;
-    int4 ids0 = make_int4(0, 0, 0, 0);
-    if constexpr (PAGED) ids0 = use_ids(fetch_ids(tile_at(g)));
-    copy_k(g, ids0, sbase);
-    copy_v(g, ids0, sbase + 2 * kSlotBytes);
-    if (nt > 1) {
-      if constexpr (PAGED) ids_v = use_ids(fetch_ids(tile_at(g + 1)));
-      copy_k(g + 1, ids_v, sbase + kSlotBytes);
-      if constexpr (PAGED)
-        if (nt > 2) ids_next = fetch_ids(tile_at(g + 2));
+    if constexpr (PAGED) {
+      const int t0 = tile_at(g);
+      const int id0 = load_id(t0);
+      copy_paged(page_rsrc(kbase, id0, t0), sbase);
+      copy_paged(page_rsrc(vbase, id0, t0), sbase + 2 * kSlotBytes);
+      if (nt > 1) {
+        id_v = load_id(tile_at(g + 1));
+        copy_paged(page_rsrc(kbase, id_v, tile_at(g + 1)), sbase + kSlotBytes);
+        if (nt > 2) raw_k = fetch_id(tile_at(g + 2));
+      }
+    } else {
+      copy_k(g, sbase);
+      copy_v(g, sbase + 2 * kSlotBytes);
+      if (nt > 1) copy_k(g + 1, sbase + kSlotBytes);
     }
   };
 
@@ -485,10 +463,17 @@ void fwd16_kernel(const FwdParams a) {
   // Issue copy x of the step's 2 * SPW copies (K slabs first).
   auto issue_copy = [&](const StepCopies& cp, int x) {
     constexpr int SPW = TileLoader<D, NW>::SPW;
-    if (x < SPW)
-      loader.load_buf(cp.kt, x, cp.kl);
-    else
-      loader.load_buf(cp.vt, x - SPW, cp.vl);
+    if constexpr (PAGED) {
+      if (x < SPW)
+        load_lds16_buf(cp.kt, ploader.voff[x], cp.kl + ploader.lds0 + x * 1024);
+      else
+        load_lds16_buf(cp.vt, ploader.voff[x - SPW], cp.vl + ploader.lds0 + (x - SPW) * 1024);
+    } else {
+      if (x < SPW)
+        loader.load_buf(cp.kt, x, cp.kl);
+      else
+        loader.load_buf(cp.vt, x - SPW, cp.vl);
+    }
   };
 
   // One pipelined step: scores of the next tile into `nx` (K slot ks),
@@ -653,15 +638,15 @@ void fwd16_kernel(const FwdParams a) {
       // end is not read before the next segment's first copies refill it.
       StepCopies cp{};
       if constexpr (PAGED) {
-        if (j + 2 < nt) {
-          const int4 ids = use_ids(ids_next);
-          copy_k(g + 2, ids, sbase + P * kSlotBytes);
-          copy_v(g + 1, ids_v, sbase + (3 - P) * kSlotBytes);
-          ids_v = ids;
-          if (j + 3 < nt) ids_next = fetch_ids(tile_at(g + 3));
-        } else if (j + 1 < nt) {
-          copy_v(g + 1, ids_v, sbase + (3 - P) * kSlotBytes);
-        }
+        // resources built from ids loaded one step earlier; a copy the
+        // segment does not have gets a resource over no rows
+        const int id_k = __builtin_amdgcn_readfirstlane(raw_k);
+        cp.kt = j + 2 < nt ? page_rsrc(kbase, id_k, tile_at(g + 2)) : buffer_rsrc(kbase, 0u);
+        cp.vt = j + 1 < nt ? page_rsrc(vbase, id_v, tile_at(g + 1)) : buffer_rsrc(vbase, 0u);
+        cp.kl = sbase + P * kSlotBytes;
+        cp.vl = sbase + (3 - P) * kSlotBytes;
+        id_v = id_k;
+        if (j + 3 < nt) raw_k = fetch_id(tile_at(g + 3));
       } else {
         // keys from the first row of K(j+2) / V(j+1) to the end (0: no copy)
         const int kleft = j + 2 < nt ? Nk - (tcur + 2 * dt) * kBC : 0;
@@ -719,14 +704,12 @@ void fwd16_kernel(const FwdParams a) {
         // The scores of the next tile are computed even when there is none
         // (last step of the segment; they are then never used), so that this
         // path is one straight instruction stream.
-        const float2 rs = fused(kl, vl, cur, nx, m2_use, std::integral_constant<bool, !PAGED>{}, cp);
+        const float2 rs = fused(kl, vl, cur, nx, m2_use, std::true_type{}, cp);
         l_run = fmaf(alpha, l_run, rs.x);
         lt_run = fmaf(alpha, lt_run, rs.y);
       } else {
-        if constexpr (!PAGED) {
 #pragma unroll
-          for (int x = 0; x < 2 * TileLoader<D, NW>::SPW; ++x) issue_copy(cp, x);
-        }
+        for (int x = 0; x < 2 * TileLoader<D, NW>::SPW; ++x) issue_copy(cp, x);
         if (nx_ok) scores(kl, nx);
       }
       cur_ok = nx_ok;
@@ -748,6 +731,8 @@ void fwd16_kernel(const FwdParams a) {
     const float lt_tot = sum_xor32(lt_run);
     float inv = lt_tot > 0.f ? 1.f / lt_tot : 0.f;
     float lse_v = l_tot > 0.f ? (m2_run + log2f(l_tot)) * kLn2 : kNegInf;
+    // a bad page seen by any wave spoils the tiles every wave used
+    if constexpr (PAGED) bad_page = __syncthreads_or(bad_page);
     if (PAGED && (bad || bad_page)) {
       inv = __builtin_nanf("");
       lse_v = __builtin_nanf("");
@@ -782,9 +767,14 @@ void fwd16_kernel(const FwdParams a) {
                    acc[db][4 * gg + 1] * inv, acc[db][4 * gg + 2] * inv,
                    acc[db][4 * gg + 3] * inv);
           }
+        // The store addresses depend on the lane only; computing them from an
+        // opaque copy of it keeps the compiler from hoisting them out of the
+        // key loop, where they would occupy registers (and spill) throughout.
+        int lane_e = lane;
+        __asm__ volatile("" : "+v"(lane_e));
 #pragma unroll
         for (int j = 0; j < kQPW * CPO / 64; ++j) {
-          const int idx = j * 64 + lane;
+          const int idx = j * 64 + lane_e;
           const int row = idx / CPO, c = idx % CPO;
           const int prow2 = qw0 + row;
           const int qrow2 = prow2 / G;
