@@ -237,7 +237,7 @@ using Parity = std::integral_constant<int, P>;
 // per-wave LDS tile carries O on its way out, so that it is stored as whole
 // rows.
 template <class E, typename OutT, int D, bool CAUSAL, int NW, bool PAGED>
-__global__ __launch_bounds__(NW * 64, 8 / NW)
+__global__ __launch_bounds__(NW * 64, (NW == 4 && D == 128) ? 1 : 8 / NW)
 void fwd16_kernel(const FwdParams a) {
   constexpr int TILE = kBC * D;                 // elements per K or V tile
   constexpr int QF = D / 16;
@@ -297,7 +297,9 @@ void fwd16_kernel(const FwdParams a) {
   const int nseg = (CAUSAL && qb_second > qb_first) ? 2 : 1;
   auto block_tiles = [&](int qb) {
     int last = Nk - 1;
-    if (CAUSAL) last = min(last, min(qb * BR + BR, nrows) / G - 1 + off);
+    // the query of the block's last packed row (a block may end inside a
+    // query's group of heads when G does not divide BR)
+    if (CAUSAL) last = min(last, (min(qb * BR + BR, nrows) - 1) / G + off);
     return tile_count(last);
   };
   int n0 = block_tiles(qb_first);
@@ -1026,32 +1028,37 @@ hipError_t launch_t(const FwdParams& p, bool causal, hipStream_t s) {
 }
 
 constexpr int kNW16 = 8;   // waves per workgroup of the 16-bit kernel (2 per SIMD)
+// A grid of fewer 8-wave workgroups than the chip has CUs leaves CUs idle and
+// runs two waves on each SIMD it uses; the same rows in 4-wave workgroups
+// (128 packed rows each) spread over twice the CUs with one wave per SIMD.
+constexpr int kNW16Small = 4;
+constexpr int kCus = 256;
 
-template <class E, typename OutT, int D, bool PAGED>
+template <class E, typename OutT, int D, bool PAGED, int NW = kNW16>
 hipError_t launch16(const FwdParams& p, bool causal, hipStream_t s) {
   if (causal)
-    hipLaunchKernelGGL((fwd16_kernel<E, OutT, D, true, kNW16, PAGED>), dim3(p.total),
-                       dim3(kNW16 * 64), 0, s, p);
+    hipLaunchKernelGGL((fwd16_kernel<E, OutT, D, true, NW, PAGED>), dim3(p.total),
+                       dim3(NW * 64), 0, s, p);
   else
-    hipLaunchKernelGGL((fwd16_kernel<E, OutT, D, false, kNW16, PAGED>), dim3(p.total),
-                       dim3(kNW16 * 64), 0, s, p);
+    hipLaunchKernelGGL((fwd16_kernel<E, OutT, D, false, NW, PAGED>), dim3(p.total),
+                       dim3(NW * 64), 0, s, p);
   return hipGetLastError();
 }
 
-template <int D>
-hipError_t dispatch_d(const FwdParams& p, const ForwardArgs& a, hipStream_t s) {
+template <int D, int NW>
+hipError_t dispatch_nw(const FwdParams& p, const ForwardArgs& a, hipStream_t s) {
   const bool c = a.causal != 0;
-  switch (a.in_dtype) {
-    case FA_BF16:
-      return a.out_dtype == FA_F32 ? launch16<BF16, float, D, false>(p, c, s)
-                                   : launch16<BF16, __bf16, D, false>(p, c, s);
-    case FA_F16:
-      return a.out_dtype == FA_F32 ? launch16<F16, float, D, false>(p, c, s)
-                                   : launch16<F16, _Float16, D, false>(p, c, s);
-    case FA_F32:
-      return launch_t<PolicyF32<D>, float, D>(p, c, s);
-  }
-  return hipErrorInvalidValue;
+  if (a.in_dtype == FA_BF16)
+    return a.out_dtype == FA_F32 ? launch16<BF16, float, D, false, NW>(p, c, s)
+                                 : launch16<BF16, __bf16, D, false, NW>(p, c, s);
+  return a.out_dtype == FA_F32 ? launch16<F16, float, D, false, NW>(p, c, s)
+                               : launch16<F16, _Float16, D, false, NW>(p, c, s);
+}
+
+template <int D>
+hipError_t dispatch_d(const FwdParams& p, const ForwardArgs& a, hipStream_t s, int nw) {
+  if (a.in_dtype == FA_F32) return launch_t<PolicyF32<D>, float, D>(p, a.causal != 0, s);
+  return nw == kNW16Small ? dispatch_nw<D, kNW16Small>(p, a, s) : dispatch_nw<D, kNW16>(p, a, s);
 }
 
 template <int D>
@@ -1094,6 +1101,7 @@ hipError_t launch_forward_paged(const ForwardPagedArgs& a, hipStream_t s) {
 
 hipError_t launch_forward(const ForwardArgs& a, hipStream_t s) {
   FwdParams p{};
+  int nw = 0;
   p.kv_splits = 1;
   p.q = a.q; p.k = a.k; p.v = a.v; p.o = a.o; p.lse = a.lse;
   p.B = a.B; p.H = a.H; p.Hkv = a.Hkv; p.Nq = a.Nq; p.Nk = a.Nk;
@@ -1104,16 +1112,24 @@ hipError_t launch_forward(const ForwardArgs& a, hipStream_t s) {
     p.units = p.n_qblocks;
     p.total = a.B * a.H * p.units;
   } else {     // per (batch, KV head): blocks of packed (query, head) rows
-    const int br = kNW16 * kQPW;
-    p.n_qblocks = static_cast<int>((int64_t{a.Nq} * p.group + br - 1) / br);
-    // causal: query blocks u and n-1-u share one workgroup
-    p.units = a.causal ? (p.n_qblocks + 1) / 2 : p.n_qblocks;
+    auto blocks = [&](int nw) {
+      const int br = nw * kQPW;
+      p.n_qblocks = static_cast<int>((int64_t{a.Nq} * p.group + br - 1) / br);
+      // causal: query blocks u and n-1-u share one workgroup
+      p.units = a.causal ? (p.n_qblocks + 1) / 2 : p.n_qblocks;
+      return int64_t{a.B} * a.Hkv * p.units;   // workgroups with work
+    };
+    nw = kNW16;
+    if (blocks(kNW16) < kCus) {
+      nw = kNW16Small;
+      blocks(kNW16Small);
+    }
     p.total = (a.B * a.Hkv + kXcds - 1) / kXcds * kXcds * p.units;
   }
   p.c = a.scale * kLog2e;
   p.off = a.Nk - a.Nq;
   if (p.total == 0) return hipSuccess;
-  return a.d == 64 ? dispatch_d<64>(p, a, s) : dispatch_d<128>(p, a, s);
+  return a.d == 64 ? dispatch_d<64>(p, a, s, nw) : dispatch_d<128>(p, a, s, nw);
 }
 
 }  // namespace fa
