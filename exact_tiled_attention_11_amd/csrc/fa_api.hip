@@ -318,6 +318,7 @@ fa_status decode_prepare(const void* q, const void* K_pool, const void* V_pool,
       fa_decode_workspace_size(B, H, Hkv, d, max_pages_per_seq, window, num_splits);
   if (check_workspace && S > 1 && (workspace == nullptr || workspace_bytes < need))
     return FA_ERR_WORKSPACE;
+  if (check_workspace && S > 1 && !aligned16(workspace)) return FA_ERR_BAD_ARG;
   fa::DecodeArgs a;
   a.q = q; a.k_pool = K_pool; a.v_pool = V_pool;
   a.block_table = block_table; a.seq_lens = seq_lens;

@@ -69,6 +69,11 @@ struct DecParams {
   int softcap_on;        // 1: scores are soft-capped
   float cap_over_scale;  // softcap / scale
   float scale_over_cap;  // scale / softcap
+  // Ragged rows (the one-query sequences of a ragged forward batch): when
+  // set, sequence b's query, O and LSE row is qo_indptr[b], and a sequence
+  // with other than exactly one query row is left to the forward kernel.
+  const int32_t* qo_indptr;
+  int total_q;
 };
 
 // Keys visible to the query of a sequence of `len` cached tokens: positions
@@ -167,6 +172,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecParams a) 
   if (split < 0) split += S;
   const int b = pq / a.Hkv, hk = pq - b * a.Hkv;
   const int G = a.group;
+  int row = b;   // query / O / LSE row of the sequence
+  if (a.qo_indptr) {
+    const int qs = a.qo_indptr[b], qe = a.qo_indptr[b + 1];
+    if (!(qs >= 0 && qe == qs + 1 && qe <= a.total_q)) return;   // whole workgroup: uniform
+    row = qs;
+  }
   const long long max_len = static_cast<long long>(a.max_pages) * kPage;
   const int len = a.seq_lens[b];
   const bool bad_len = len < 0 || len > max_len;
@@ -192,7 +203,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecParams a) 
   const int hs = lane & 15, grp = lane >> 4;
   typename E::vec8 qop[Geo::NC];
   {
-    const uint16_t* qrow = a.q + (static_cast<int64_t>(b) * a.H + hk * G + hs) * D + 8 * grp;
+    const uint16_t* qrow = a.q + (static_cast<int64_t>(row) * a.H + hk * G + hs) * D + 8 * grp;
 #pragma unroll
     for (int c = 0; c < Geo::NC; ++c) {
       uint4 u = make_uint4(0, 0, 0, 0);
@@ -367,8 +378,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(const DecParams a) 
     const int h = hk * G + n;
     const int64_t bh = static_cast<int64_t>(b) * a.H + h;
     if (final_out) {
-      store1(static_cast<OutT*>(a.o) + bh * D + dd, o);
-      if (dd == 0) a.lse[bh] = lse;
+      const int64_t rh = static_cast<int64_t>(row) * a.H + h;
+      store1(static_cast<OutT*>(a.o) + rh * D + dd, o);
+      if (dd == 0) a.lse[rh] = lse;
     } else {
       a.part_o[(bh * a.max_splits + split) * D + dd] = o;
       if (dd == 0) a.part_lse[bh * a.max_splits + split] = lse;
@@ -400,6 +412,37 @@ struct MergeParams {
 };
 
 constexpr int kMergeMaxS = 1024;
+
+// acc[i] += w_c o_c[x0 + i] for c = 0 .. n-1 in index order (i < V), the
+// loads of 16 parts issued together.
+template <int V>
+__device__ __forceinline__ void merge_parts(const float* o_r, const float* w, int n, int d,
+                                            int x0, float* acc) {
+  for (int c0 = 0; c0 < n; c0 += 16) {
+    float buf[16][V];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const float* src = o_r + min(c0 + k, n - 1) * d + x0;
+      if constexpr (V == 2) {
+        const float2 t = *reinterpret_cast<const float2*>(src);
+        buf[k][0] = t.x;
+        buf[k][1] = t.y;
+      } else {
+        buf[k][0] = *src;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const bool on = c0 + k < n;
+      const float wk = w[min(c0 + k, n - 1)];
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        const float t = fmaf(wk, buf[k][i], acc[i]);
+        acc[i] = on ? t : acc[i];
+      }
+    }
+  }
+}
 
 template <typename OutT, bool DECODE>
 __global__ __launch_bounds__(256) void merge_kernel(const MergeParams a) {
@@ -458,16 +501,26 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams a) {
   z += we;
   __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // own wave's LDS writes
   const float inv = 1.f / z;
-  for (int x = lane; x < a.d; x += 64) {
-    float acc = 0.f;
-    if (DECODE) {
-#pragma unroll 8
-      for (int c = 0; c < n; ++c) acc = fmaf(wsh[wave][c], o_r[c * a.d + x], acc);
-    } else {
+  if (DECODE) {
+    // d = 64 or 128: lane l sums elements l * d / 64 .. +d / 64 - 1 (one or
+    // two) over the parts in index order. The part loads go out 16 at a time
+    // (a short last batch re-reads the last part and skips its terms), so a
+    // row of up to 64 parts waits for at most four round trips.
+    float acc[2] = {0.f, 0.f};
+    if (a.d == 128)
+      merge_parts<2>(o_r, wsh[wave], n, 128, 2 * lane, acc);
+    else
+      merge_parts<1>(o_r, wsh[wave], n, 64, lane, acc);
+    const int v = a.d >> 6;
+    store1(out + v * lane, acc[0] * inv);
+    if (v == 2) store1(out + v * lane + 1, acc[1] * inv);
+  } else {
+    for (int x = lane; x < a.d; x += 64) {
+      float acc = 0.f;
       for (int c = 0; c < n; ++c) acc = fmaf(wsh[wave][c], o_r[c * a.d + x], acc);
       if (a.o_extra) acc = fmaf(we, a.o_extra[r * a.d + x], acc);
+      store1(out + x, acc * inv);
     }
-    store1(out + x, acc * inv);
   }
   if (lane == 0) a.lse[r] = M + logf(z);
 }
@@ -563,6 +616,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   p.softcap_on = a.softcap > 0.f ? 1 : 0;
   p.cap_over_scale = a.softcap > 0.f ? a.softcap / a.scale : 0.f;
   p.scale_over_cap = a.softcap > 0.f ? a.scale / a.softcap : 0.f;
+  p.qo_indptr = nullptr;
+  p.total_q = 0;
   const int G = a.H / a.Hkv;
   const dim3 grid(static_cast<unsigned>(a.max_splits * a.B * a.Hkv));
   hipError_t e;
@@ -593,6 +648,37 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   m.o_extra = nullptr;
   m.lse_extra = nullptr;
   return merge_dispatch<true>(m, a.out_dtype, s);
+}
+
+hipError_t launch_decode_rows(const ForwardPagedArgs& a, hipStream_t s) {
+  if (a.B == 0) return hipSuccess;
+  DecParams p;
+  p.q = static_cast<const uint16_t*>(a.q);
+  p.k_pool = static_cast<const uint16_t*>(a.k_pool);
+  p.v_pool = static_cast<const uint16_t*>(a.v_pool);
+  p.block_table = a.block_table;
+  p.seq_lens = a.kv_lens;
+  p.o = a.o;
+  p.lse = a.lse;
+  p.part_o = nullptr;
+  p.part_lse = nullptr;
+  p.B = a.B; p.H = a.H; p.Hkv = a.Hkv;
+  p.max_pages = a.max_pages; p.num_pages = a.num_pages;
+  p.num_splits = 1; p.max_splits = 1;   // one workgroup per (sequence, KV head)
+  p.group = a.H / a.Hkv;
+  p.c = a.scale * kLog2e;
+  p.window = 0;
+  p.softcap_on = 0;
+  p.cap_over_scale = 0.f;
+  p.scale_over_cap = 0.f;
+  p.qo_indptr = a.qo_indptr;
+  p.total_q = a.total_q;
+  const dim3 grid(static_cast<unsigned>(a.B * a.Hkv));
+  if (a.dtype == FA_BF16)
+    return a.out_dtype == FA_F32 ? launch_decode_d<BF16, float>(p, a.d, p.group, grid, s)
+                                 : launch_decode_d<BF16, __bf16>(p, a.d, p.group, grid, s);
+  return a.out_dtype == FA_F32 ? launch_decode_d<F16, float>(p, a.d, p.group, grid, s)
+                               : launch_decode_d<F16, _Float16>(p, a.d, p.group, grid, s);
 }
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {

@@ -82,6 +82,8 @@ struct FwdParams {
   int kv_splits;
   float* part_o;
   float* part_lse;
+  // 1: sequences with exactly one query row are left to the decode kernel.
+  int skip_single;
 };
 
 // ---------------------------------------------------------------------------
@@ -269,6 +271,7 @@ void fwd16_kernel(const FwdParams a) {
     const int qs = a.qo_indptr ? a.qo_indptr[b] : 0;
     const int qe = a.qo_indptr ? a.qo_indptr[b + 1] : a.total_q;
     if (qs < 0 || qe < qs || qe > a.total_q) return;   // rows unknown: nothing is written
+    if (a.skip_single && qe == qs + 1) return;           // a decode row: the decode kernel's
     Nq = qe - qs;
     q_row0 = qs;
     Nk = a.kv_lens ? a.kv_lens[b] : a.fixed_kv_len;
@@ -1096,6 +1099,15 @@ hipError_t launch_forward_paged(const ForwardPagedArgs& a, hipStream_t s) {
   p.total_q = a.total_q;
   p.max_q_len = a.max_q_len;
   if (p.total == 0) return hipSuccess;
+  // Sequences with a single query row (decode tokens in a mixed batch) go
+  // through the split-KV decode kernel's page streaming instead: here such a
+  // row would keep a whole workgroup of 8 waves waiting on every key tile
+  // for the work of one wave.
+  p.skip_single = !partial && a.qo_indptr && a.kv_lens && p.group <= 16 && a.max_q_len >= 1;
+  if (p.skip_single) {
+    const hipError_t e = launch_decode_rows(a, s);
+    if (e != hipSuccess) return e;
+  }
   return a.d == 64 ? dispatch_paged_d<64>(p, a, s) : dispatch_paged_d<128>(p, a, s);
 }
 

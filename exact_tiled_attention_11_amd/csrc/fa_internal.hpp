@@ -85,6 +85,10 @@ hipError_t decode_scratch(void** ptr);
 hipError_t launch_forward(const ForwardArgs& a, hipStream_t s);
 hipError_t launch_forward_paged(const ForwardPagedArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+// The one-query sequences of a ragged batch (qo_indptr[b + 1] - qo_indptr[b]
+// == 1) through the decode kernel, one workgroup per (sequence, KV head);
+// needs qo_indptr and kv_lens, H / Hkv <= 16, no partial mode.
+hipError_t launch_decode_rows(const ForwardPagedArgs& a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 
 }  // namespace fa

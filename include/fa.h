@@ -131,6 +131,11 @@ fa_status fa_forward(const void* Q, const void* K, const void* V, void* O,
  * sees key j iff j <= i + kv_lens[b] - q_len_b (bottom-right alignment, as
  * fa_forward); a decode step is simply q_len_b = 1. Otherwise as fa_forward:
  * the same arithmetic, scale, GQA mapping and outputs per (row, head).
+ * Sequences with exactly one query row are computed as fa_decode_paged
+ * computes a sequence with one chunk, by the decode kernel's page streaming
+ * (one workgroup per sequence and KV head, in a launch of their own before
+ * the other rows'); their results agree with the tiled kernel's to the
+ * stated tolerance, not bit for bit. This applies when H / Hkv <= 16.
  *
  * Layouts (row-major, contiguous):
  *   Q            [total_q, H, d]                      dtype
@@ -278,9 +283,9 @@ size_t fa_decode_workspace_size(int B, int H, int Hkv, int d,
  *   O            [B, H, d]                          out_dtype (dtype or FA_F32)
  *   LSE          [B, H]                  float
  *   workspace    >= fa_decode_workspace_size(B, H, Hkv, d, max_pages_per_seq,
- *                0, num_splits) bytes of device memory (may be NULL when the
- *                slot count is 1); contents on entry are ignored, on exit
- *                unspecified.
+ *                0, num_splits) bytes of device memory, 16-byte aligned (may
+ *                be NULL when the slot count is 1); contents on entry are
+ *                ignored, on exit unspecified.
  *
  * Supported: dtype in {FA_F16, FA_BF16}; d in {64, 128}; page_size ==
  * FA_PAGE_SIZE; 0 <= num_splits <= FA_MAX_SPLITS; H % Hkv == 0 and

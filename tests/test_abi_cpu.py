@@ -245,6 +245,8 @@ def test_decode_workspace_checks():
     assert dec(max_pages=200, ptrs=p, ws=FAKE, ws_bytes=need - 1) == WS
     need4 = fa.decode_workspace_size(2, 8, 2, 128, 4, 0, 4)
     assert dec(ptrs=p, splits=4, ws=FAKE, ws_bytes=need4 - 4) == WS
+    # a workspace that is large enough but not 16-byte aligned
+    assert dec(max_pages=200, ptrs=p, ws=ctypes.c_void_p(0x1008), ws_bytes=need) == ARG
 
 
 def plan_by_hand(lens, Hkv, max_pages, window=0, fixed=0):
