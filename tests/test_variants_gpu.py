@@ -273,6 +273,46 @@ def test_forward_paged_contract_violations_give_nan():
             assert torch.isnan(o[r0:r1]).all() and torch.isnan(l[r0:r1]).all()
 
 
+def test_forward_paged_single_query_rows_are_the_decode():
+    """One-query sequences of a ragged batch are computed by the decode
+    kernel: bit for bit what fa_decode_paged gives for them with one chunk,
+    and the other sequences as before."""
+    q_lens, kv_lens = [1, 300, 1, 1, 2, 1], [4100, 300, 1, 0, 900, 77]
+    H, Hkv, d = 32, 8, 128
+    ri = inputs.ragged_paged_inputs(q_lens, kv_lens, H, Hkv, d, seed=54)
+    for causal in (False, True):
+        say(f"forward_paged one-query rows causal={causal}")
+        o, l = gpu_forward_paged(ri, causal, torch.float32)
+        rows = [int(ri.qo_indptr[b]) for b in range(len(q_lens)) if q_lens[b] == 1]
+        seqs = [b for b in range(len(q_lens)) if q_lens[b] == 1]
+        od, ld = fa.decode_paged(ri.q[rows].contiguous().to(DEV), ri.k_pool.to(DEV),
+                                 ri.v_pool.to(DEV), ri.block_table[seqs].contiguous().to(DEV),
+                                 ri.kv_lens[seqs].contiguous().to(DEV), num_splits=1,
+                                 out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(o[rows], od) and torch.equal(l[rows], ld)
+        ro, rl = oracle.attention_ragged_paged(ri.q, ri.qo_indptr, ri.k_pool, ri.v_pool,
+                                               ri.block_table, ri.kv_lens, 1 / math.sqrt(d),
+                                               causal)
+        assert_lowp_acc("one-query rows", np64(o), ro)
+        assert_lse("one-query rows", np64(l), rl)
+
+
+def test_forward_paged_single_query_contract_violations_give_nan():
+    q_lens, kv_lens = [1, 1, 1, 1, 3], [100, 100, 100, 100, 100]
+    ri = inputs.ragged_paged_inputs(q_lens, kv_lens, 8, 2, 128, seed=55)
+    ri.block_table[1, 3] = ri.k_pool.shape[0]   # page id outside the pool
+    ri.kv_lens[2] = 10_000                      # longer than the block table allows
+    ri.kv_lens[3] = -5
+    say("forward_paged one-query contract violations")
+    for causal in (False, True):
+        o, l = gpu_forward_paged(ri, causal, torch.float32)
+        assert torch.isfinite(o[0]).all() and torch.isfinite(l[0]).all()
+        assert torch.isfinite(o[4:]).all() and torch.isfinite(l[4:]).all()
+        for r in (1, 2, 3):
+            assert torch.isnan(o[r]).all() and torch.isnan(l[r]).all()
+
+
 # ---------------------------------------------------------------------------
 # Cascade: a shared prefix attended once, merged with each sequence's suffix.
 # ---------------------------------------------------------------------------
