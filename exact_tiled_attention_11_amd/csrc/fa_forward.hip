@@ -239,13 +239,15 @@ using Parity = std::integral_constant<int, P>;
 // per-wave LDS tile carries O on its way out, so that it is stored as whole
 // rows.
 template <class E, typename OutT, int D, bool CAUSAL, int NW, bool PAGED>
-__global__ __launch_bounds__(NW * 64, (NW == 4 && D == 128) ? 1 : 8 / NW)
+__global__ __launch_bounds__(NW * 64, (NW == 4 && D == 128) ? 1 : NW == 2 ? 2 : 8 / NW)
 void fwd16_kernel(const FwdParams a) {
   constexpr int TILE = kBC * D;                 // elements per K or V tile
   constexpr int QF = D / 16;
   constexpr int DB = D / 32;
   constexpr int BR = NW * kQPW;
   using V8 = typename E::vec8;
+  // the paged share of a tile (instantiated for the dense layout too, unused)
+  using PLoader = PagedTileLoader<D, PAGED ? NW : 8>;
   __shared__ __attribute__((aligned(16))) uint16_t smem[4][TILE];   // K0 K1 V0 V1
   // 16-bit outputs: each wave's 32 x D tile of O passes through LDS so that
   // it is stored as whole rows.
@@ -335,7 +337,7 @@ void fwd16_kernel(const FwdParams a) {
   // the sequence bad (NaN output, agreed over all waves at the end).
   const int32_t* table = PAGED ? a.block_table + static_cast<int64_t>(b) * a.max_pages : nullptr;
   const int last_page = Nk > 0 ? (Nk - 1) / kPageTokens : 0;
-  const int wave_page = PagedTileLoader<D, NW>::page_of_wave(wave);
+  const int wave_page = PLoader::page_of_wave(wave);
   bool bad_page = false;
   // The id as loaded (a vector register, the same in every lane); made
   // wave-uniform only where it is used, a step later, so that the load's
@@ -386,7 +388,7 @@ void fwd16_kernel(const FwdParams a) {
   constexpr uint32_t kSlotBytes = TILE * 2;   // slot x of smem starts x * kSlotBytes in
 
   const TileLoader<D, NW> loader(kv_rs, wave, lane);
-  const PagedTileLoader<D, NW> ploader(kv_rs, wave, lane);
+  const PLoader ploader(kv_rs, wave, lane);
   // Paged: page id of the tile whose V is copied next (= the K tile of the
   // previous step) and, as fetched, of the K tile copied next.
   int id_v = 0, raw_k = 0;
@@ -395,7 +397,7 @@ void fwd16_kernel(const FwdParams a) {
   // This wave's slabs of a paged tile, from a page resource.
   auto copy_paged = [&](i32x4 rsrc, uint32_t dst) {
 #pragma unroll
-    for (int r = 0; r < PagedTileLoader<D, NW>::SPW; ++r)
+    for (int r = 0; r < PLoader::SPW; ++r)
       load_lds16_buf(rsrc, ploader.voff[r], dst + ploader.lds0 + r * 1024);
   };
   // First copies of a segment whose first step is g: K and V of step g into
@@ -1033,8 +1035,11 @@ hipError_t launch_t(const FwdParams& p, bool causal, hipStream_t s) {
 constexpr int kNW16 = 8;   // waves per workgroup of the 16-bit kernel (2 per SIMD)
 // A grid of fewer 8-wave workgroups than the chip has CUs leaves CUs idle and
 // runs two waves on each SIMD it uses; the same rows in 4-wave workgroups
-// (128 packed rows each) spread over twice the CUs with one wave per SIMD.
+// (128 packed rows each) spread over twice the CUs with one wave per SIMD,
+// and in 2-wave workgroups (64 rows) over four times as many when even the
+// 4-wave grid is short of the CU count and the 2-wave one is not over it.
 constexpr int kNW16Small = 4;
+constexpr int kNW16Tiny = 2;
 constexpr int kCus = 256;
 
 template <class E, typename OutT, int D, bool PAGED, int NW = kNW16>
@@ -1061,6 +1066,7 @@ hipError_t dispatch_nw(const FwdParams& p, const ForwardArgs& a, hipStream_t s) 
 template <int D>
 hipError_t dispatch_d(const FwdParams& p, const ForwardArgs& a, hipStream_t s, int nw) {
   if (a.in_dtype == FA_F32) return launch_t<PolicyF32<D>, float, D>(p, a.causal != 0, s);
+  if (nw == kNW16Tiny) return dispatch_nw<D, kNW16Tiny>(p, a, s);
   return nw == kNW16Small ? dispatch_nw<D, kNW16Small>(p, a, s) : dispatch_nw<D, kNW16>(p, a, s);
 }
 
@@ -1134,7 +1140,12 @@ hipError_t launch_forward(const ForwardArgs& a, hipStream_t s) {
     nw = kNW16;
     if (blocks(kNW16) < kCus) {
       nw = kNW16Small;
-      blocks(kNW16Small);
+      // 2-wave workgroups only while each still gets a CU of its own: two
+      // sharing a CU take twice as long as one 4-wave workgroup of theirs
+      if (blocks(kNW16Small) < kCus && blocks(kNW16Tiny) <= kCus)
+        nw = kNW16Tiny;
+      else
+        blocks(kNW16Small);
     }
     p.total = (a.B * a.Hkv + kXcds - 1) / kXcds * kXcds * p.units;
   }

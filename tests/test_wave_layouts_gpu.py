@@ -1,8 +1,9 @@
-"""The dense 16-bit forward runs in workgroups of 8 waves (256 packed rows)
+"""The dense 16-bit forward runs in workgroups of 8 waves (256 packed rows),
 or, when that grid would have fewer workgroups than the chip has CUs, of 4
-waves (128 rows). Both layouts are compared here with the float64 oracle on
-ragged shapes on either side of the switch: tails of query blocks and key
-tiles, GQA packing, bottom-right causal masks with Nq < Nk and Nq > Nk.
+waves (128 rows), or of 2 waves (64 rows) when even the 4-wave grid would.
+All three layouts are compared here with the float64 oracle on ragged shapes
+on either side of the switches: tails of query blocks and key tiles, GQA
+packing, bottom-right causal masks with Nq < Nk and Nq > Nk.
 """
 
 import math
@@ -25,11 +26,15 @@ CUS = 256
 
 def waves_per_workgroup(B, Hkv, Nq, G, causal):
     """The host's rule: 8 waves unless that grid has fewer than 256 working
-    workgroups (blocks of 32 rows per wave, causal blocks paired)."""
-    def units(nw):
+    workgroups (blocks of 32 rows per wave, causal blocks paired); then 4,
+    or 2 when the 4-wave grid is short of 256 too and the 2-wave grid is not
+    over 256."""
+    def wgs(nw):
         nqb = -(-(Nq * G) // (nw * 32))
-        return (nqb + 1) // 2 if causal else nqb
-    return 8 if B * Hkv * units(8) >= CUS else 4
+        return B * Hkv * ((nqb + 1) // 2 if causal else nqb)
+    if wgs(8) >= CUS:
+        return 8
+    return 2 if wgs(4) < CUS and wgs(2) <= CUS else 4
 
 
 # B, H, Hkv, Nq, Nk, d, dtype, causal
@@ -37,26 +42,33 @@ CASES = [
     (4, 32, 16, 1000, 1000, 128, "bf16", True),    # 256 units: 8 waves
     (2, 64, 16, 1000, 1000, 64, "f16", False),     # G = 4, 8 waves
     (5, 17, 17, 600, 600, 128, "bf16", True),      # 170 units of 8 waves: 4 waves
+    (2, 32, 32, 1500, 1500, 128, "bf16", True),    # 192 units of 8 waves: 4 waves
+    (1, 8, 8, 1000, 1000, 128, "f16", True),       # 16 / 32 / 64 units: 2 waves
+    (1, 16, 4, 500, 700, 64, "bf16", False),       # G = 4, Nq < Nk, non-causal: 2 waves
     (1, 32, 32, 2048, 2048, 64, "bf16", False),    # exactly 256 units: 8 waves
     (8, 32, 8, 700, 1500, 128, "bf16", True),      # Nq < Nk, G = 4, 8 waves
     (2, 32, 8, 700, 1500, 64, "f16", True),        # the same, 4 waves
+    (1, 32, 8, 700, 1500, 64, "f16", True),        # the same, 2 waves
     (8, 16, 16, 1100, 300, 128, "f16", True),      # Nq > Nk: first rows see no key, 8 waves
     (2, 16, 16, 1100, 300, 128, "bf16", True),     # the same, 4 waves
+    (1, 16, 16, 1100, 300, 128, "f16", True),      # the same, 2 waves
     (3, 48, 16, 777, 777, 128, "bf16", False),     # G = 3, 8 waves
     (1, 48, 16, 777, 777, 128, "f16", False),      # G = 3, 4 waves
     # Causal blocks that end inside a query's group of heads (G does not
     # divide the block), where that query's last visible key opens a new key
     # tile: the block must stream that tile too.
     (8, 48, 8, 400, 422, 128, "bf16", True),       # G = 6, 8 waves
-    (2, 48, 8, 400, 422, 64, "f16", True),         # G = 6, 4 waves
+    (4, 48, 8, 400, 422, 128, "f16", True),        # G = 6, 4 waves
+    (1, 48, 8, 400, 422, 64, "bf16", True),        # G = 6, 2 waves
     (16, 24, 8, 300, 343, 128, "f16", True),       # G = 3, 8 waves
-    (2, 24, 8, 300, 343, 128, "bf16", True),       # G = 3, 4 waves
+    (8, 24, 8, 300, 343, 128, "bf16", True),       # G = 3, 4 waves
+    (2, 24, 8, 300, 343, 128, "bf16", True),       # G = 3, 2 waves
 ]
 
 
-def test_cases_cover_both_layouts():
+def test_cases_cover_all_layouts():
     lay = [waves_per_workgroup(B, Hkv, Nq, H // Hkv, c) for B, H, Hkv, Nq, Nk, d, dt, c in CASES]
-    assert lay == [8, 8, 4, 8, 8, 4, 8, 4, 8, 4, 8, 4, 8, 4]
+    assert lay == [8, 8, 4, 4, 2, 2, 8, 8, 4, 2, 8, 4, 2, 8, 4, 8, 4, 2, 8, 4, 2]
 
 
 def block_tile_counts(Nq, Nk, G, BR):
@@ -73,7 +85,7 @@ def block_tile_counts(Nq, Nk, G, BR):
 def test_block_tiles_reach_the_last_rows_query():
     # brute force: the last tile any row of the block sees
     for Nq, Nk, G in [(400, 422, 6), (300, 343, 3), (124, 18, 6), (77, 500, 5)]:
-        for BR in (128, 256):
+        for BR in (64, 128, 256):
             want = []
             for qb in range(-(-(Nq * G) // BR)):
                 rows = range(qb * BR, min(qb * BR + BR, Nq * G))
