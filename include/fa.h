@@ -266,8 +266,9 @@ size_t fa_decode_workspace_size(int B, int H, int Hkv, int d,
  * a block table, the fill of the final page expressed here by the sequence
  * length). Table
  * entries past the last used page are never read. The tokens are cut into
- * fa_decode_num_splits(seq_lens[b], num_splits) near-equal, page-aligned
- * chunks; each chunk's partial (o = acc / l, lse = m + ln l) is computed
+ * the near-equal, page-aligned chunks of the split plan above (as many as
+ * fa_decode_plan returns for the sequence, num_splits when it is > 0);
+ * each chunk's partial (o = acc / l, lse = m + ln l) is computed
  * independently and the partials are merged by the merge rule
  * ("Decode attention and Flash-Decoding"). All query heads that share a KV
  * head are processed together so each loaded K/V row serves all of them
