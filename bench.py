@@ -331,7 +331,8 @@ def bench_long_prefill(torch, fa, inputs, reps=10):
     torch.cuda.empty_cache()
     return {"workload": LONG, "config": {k_: p[k_] for k_ in ("B", "H", "Hkv", "N", "d")} |
             {"causal": True, "q_scale": p["q_scales"][0]},
-            "ms_mean": float(ms.mean()), "ms_min": float(ms.min()), "calls": reps,
+            "ms_mean": float(ms.mean()), "ms_median": float(np.median(ms)),
+            "ms_min": float(ms.min()), "calls": reps,
             "algorithmic_flop": fl, "value": tf, "unit": "TFLOP/s", "bound": "mfma",
             "peak": MFMA_BF16_PEAK_TFLOPS, "frac": tf / MFMA_BF16_PEAK_TFLOPS,
             "traffic": tr["hbm_bytes_per_launch"] if tr else None}
@@ -612,12 +613,14 @@ def main():
             "traffic": tr_pre["hbm_bytes_per_launch"] if tr_pre else None,
             "traffic_detail": tr_pre,
             "kernel": "fwd16_kernel<BF16, bf16 out, d=128, causal, 8 waves, paired query blocks>",
-            "ms_mean": float(pre_ms.mean()), "ms_min": float(pre_ms.min()),
+            "ms_mean": float(pre_ms.mean()), "ms_median": float(np.median(pre_ms)),
+            "ms_min": float(pre_ms.min()),
             "algorithmic_flop_per_launch": flops},
         "decode": None if dec_gbps is None else {
             "value": dec_gbps, "unit": "GB/s", "bound": "hbm", "peak": HBM_PEAK_GBPS,
             "frac": dec_gbps / HBM_PEAK_GBPS, "ms_mean": float(dec_ms.mean()),
-            "ms_min": float(dec_ms.min()), "kv_bytes": kv_bytes,
+            "ms_median": float(np.median(dec_ms)), "ms_min": float(dec_ms.min()),
+            "kv_bytes": kv_bytes,
             "timed": "decode kernel + merge kernel",
             "stream_read": read_rate,
             "frac_of_stream_read": dec_gbps / read_rate["value"] if read_rate else None,
