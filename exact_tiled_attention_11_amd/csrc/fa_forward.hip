@@ -12,7 +12,8 @@
 // causal diagonal are never loaded.
 //
 // Work decomposition of the bf16/fp16 kernel (one workgroup = 8 waves, two
-// per SIMD, 32 query rows per wave; one key tile = 64 keys):
+// per SIMD, 32 query rows per wave; 4 or 2 waves when the grid would not fill
+// the chip; one key tile = 64 keys):
 //   * Scores are computed transposed, S^T = K Q^T, so that every lane owns ONE
 //     query row (l % 32) and 32 of the tile's keys: the row max and row sum
 //     are in-lane reductions plus one exchange with lane l ^ 32, and the
