@@ -82,8 +82,44 @@ def _draw_decode(n, seed):
     return cases
 
 
-DENSE = _draw_dense(24, 7321)
-PAGED = _draw_paged(12, 7322)
+def _draw_dense_large(n, seed):
+    """Batches large enough to reach all three workgroup layouts (8, 4 and 2
+    waves), with ragged query blocks and key tiles."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        hkv = int(rng.choice([2, 4, 8]))
+        g = int(rng.choice([2, 3, 4, 6]))
+        d = int(rng.choice([64, 128]))
+        dt = str(rng.choice(["bf16", "f16"]))
+        nq = int(rng.integers(300, 1000))
+        nk = [nq, int(rng.integers(1, 1300))][int(rng.choice(2, p=[0.6, 0.4]))]
+        cases.append((int(rng.integers(1, 7)), hkv * g, hkv, nq, nk, d, dt,
+                      bool(rng.integers(0, 2)), 5000 + i))
+    return cases
+
+
+def _draw_paged_decode_heavy(n, seed):
+    """Ragged batches in which most sequences have one query row (computed
+    by the decode kernel) beside a few longer ones (the tiled kernel)."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        hkv = int(rng.choice([1, 2, 8]))
+        g = int(rng.choice([1, 3, 4, 8, 16]))
+        d = int(rng.choice([64, 128]))
+        dt = str(rng.choice(["bf16", "f16"]))
+        nseq = int(rng.integers(4, 12))
+        q_lens = [1 if rng.random() < 0.75 else int(rng.integers(2, 300)) for _ in range(nseq)]
+        kv_lens = [[0, 1, int(rng.integers(1, 5000))][int(rng.choice(3, p=[0.05, 0.05, 0.9]))]
+                   for _ in range(nseq)]
+        kv_lens = [max(k, q) for k, q in zip(kv_lens, q_lens)]
+        cases.append((hkv * g, hkv, d, dt, q_lens, kv_lens, bool(rng.integers(0, 2)), 6000 + i))
+    return cases
+
+
+DENSE = _draw_dense(24, 7321) + _draw_dense_large(10, 7324)
+PAGED = _draw_paged(12, 7322) + _draw_paged_decode_heavy(8, 7325)
 DECODE = _draw_decode(12, 7323)
 
 
