@@ -156,14 +156,12 @@ struct TileLoader {
     }
   }
 
-  // Buffer resource of the tile whose first row is b0, with `left` keys from
-  // there to the end of the sequence: its rows past the last key (all rows
-  // when left <= 0) are out of range and copy as zeros without a memory
-  // access. (rows - 1) * rs + D <= Nk * rs elements, below 2^31 (the API's
-  // size limit), so the byte count fits 32 bits.
-  static __device__ __forceinline__ i32x4 rsrc(const uint16_t* b0, int rs, int left) {
-    const int rows = min(left, kBC);
-    return buffer_rsrc(b0, rows > 0 ? static_cast<uint32_t>((rows - 1) * rs + D) * 2u : 0u);
+  // Bytes a buffer resource whose base is a tile's first row must cover for
+  // `rows` (1..kBC) rows of keys: rows past the range are out of range and
+  // copy as zeros without a memory access. (rows - 1) * rs + D <= Nk * rs
+  // elements, below 2^31 (the API's size limit), so the count fits 32 bits.
+  static __device__ __forceinline__ uint32_t rsrc_bytes(int rs, int rows) {
+    return static_cast<uint32_t>((rows - 1) * rs + D) * 2u;
   }
   // Slab r of this wave's share of the tile of resource t.
   __device__ __forceinline__ void load_buf(i32x4 t, int r, uint32_t lds) const {
@@ -590,18 +588,33 @@ void fwd16_kernel(const FwdParams a) {
                           : CAUSAL ? min(Nk - 1, (min(qw0 + kQPW, nrows) - 1) / G + off)
                                    : Nk - 1;
     const int lim_row = CAUSAL ? min(Nk - 1, qrow + off) : Nk - 1;   // this lane's last key
+    // A tile starting at key k0 holds keys some row of this wave must not see
+    // (past the last key, or past the diagonal of the wave's first row) iff
+    // k0 > mask_k0.
+    const int mask_k0 = __builtin_amdgcn_readfirstlane(
+        CAUSAL ? min(Nk - kBC, qw0 / G + off - kBC + 1) : Nk - kBC);
 
     // The LDS rings restart with every segment (its step j uses the slots of
     // parity j & 1): first copies, then this segment's query fragments.
     segment_copies(g, nt);
-    // Contiguous layout: key tile of the current step and the first row of
-    // its K and V; the tiles move up by one per step through the first block
-    // and down through the second.
+    // Key tile of the current step: up by one per step through the first
+    // block and down through the second.
     const int dt = seg == 0 ? 1 : -1;
-    const int64_t dstep = static_cast<int64_t>(dt) * kBC * kv_rs;
     int tcur = nt > 0 ? tile_at(g) : 0;
-    const uint16_t* kcur = kbase + static_cast<int64_t>(tcur) * kBC * kv_rs;
-    const uint16_t* vcur = vbase + static_cast<int64_t>(tcur) * kBC * kv_rs;
+    // Contiguous layout: at step j, the K tile copied (that of step j + 2)
+    // starts at k2 and the V tile (of step j + 1) at v1. Every tile of a
+    // segment is whole but the one holding the last key when Nk is not a
+    // multiple of the tile, streamed at step j_rag of the segment (if at all):
+    // its resource covers only the rows up to the last key.
+    const int64_t dstep = static_cast<int64_t>(dt) * kBC * kv_rs;
+    const uint16_t* k2 = kbase + static_cast<int64_t>(tcur + 2 * dt) * kBC * kv_rs;
+    const uint16_t* v1 = vbase + static_cast<int64_t>(tcur + dt) * kBC * kv_rs;
+    const uint32_t full_bytes = TileLoader<D, NW>::rsrc_bytes(kv_rs32, kBC);
+    const int t_rag = (Nk % kBC) ? Nk / kBC : -1;
+    int j_rag = t_rag < 0 ? -1 : dt > 0 ? t_rag - tcur : tcur - t_rag;
+    if (j_rag >= nt) j_rag = -1;
+    const uint32_t rag_bytes =
+        t_rag < 0 ? full_bytes : TileLoader<D, NW>::rsrc_bytes(kv_rs32, Nk - t_rag * kBC);
     {
       const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
                            (q_row0 + qrow) * q_rs +
@@ -656,24 +669,25 @@ void fwd16_kernel(const FwdParams a) {
         id_v = id_k;
         if (j + 3 < nt) raw_k = fetch_id(tile_at(g + 3));
       } else {
-        // keys from the first row of K(j+2) / V(j+1) to the end (0: no copy)
-        const int kleft = j + 2 < nt ? Nk - (tcur + 2 * dt) * kBC : 0;
-        const int vleft = j + 1 < nt ? Nk - (tcur + dt) * kBC : 0;
-        cp.kt = TileLoader<D, NW>::rsrc(kcur + 2 * dstep, kv_rs32, kleft);
-        cp.vt = TileLoader<D, NW>::rsrc(vcur + dstep, kv_rs32, vleft);
+        // a copy the segment does not have gets a resource over no rows
+        const uint32_t kb = j + 2 < nt ? (j + 2 == j_rag ? rag_bytes : full_bytes) : 0u;
+        const uint32_t vb = j + 1 < nt ? (j + 1 == j_rag ? rag_bytes : full_bytes) : 0u;
+        cp.kt = buffer_rsrc(k2, kb);
+        cp.vt = buffer_rsrc(v1, vb);
         cp.kl = sbase + P * kSlotBytes;
         cp.vl = sbase + (3 - P) * kSlotBytes;
-        tcur += dt;
-        kcur += dstep;
-        vcur += dstep;
+        k2 += dstep;
+        v1 += dstep;
       }
-      const int k0 = tile_at(g) * kBC;
-      const bool nx_ok = j + 1 < nt && tile_at(g + 1) * kBC <= wave_last;
+      // first key of this step's tile; whether this wave has rows that see
+      // the next step's tile
+      const int k0 = (PAGED ? tile_at(g) : tcur) * kBC;
+      const bool nx_ok = j + 1 < nt && (PAGED ? tile_at(g + 1) : tcur + dt) * kBC <= wave_last;
+      if constexpr (!PAGED) tcur += dt;
       constexpr uint32_t kl = 1 - P;   // K slot of step j + 1
       constexpr uint32_t vl = 2 + P;   // V slot of step j
       if (cur_ok) {
-        const bool need_mask = (k0 + kBC > Nk) || (CAUSAL && k0 + kBC - 1 > qw0 / G + off);
-        if (need_mask) {
+        if (k0 > mask_k0) {
           const int rel = lim_row - k0 - 4 * khi;
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
