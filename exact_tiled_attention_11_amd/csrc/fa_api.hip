@@ -46,7 +46,12 @@ int64_t forward16_grid(int64_t B, int64_t Hkv, int64_t group, int64_t max_q, boo
 }
 
 // The kernels move data in 16-byte vectors.
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+// 16-byte aligned and inside the 48-bit GPU virtual address space (the base
+// field of a buffer resource holds address bits 0..47 and nothing above).
+bool aligned16(const void* p) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return (a & 15u) == 0 && (static_cast<uint64_t>(a) >> 48) == 0;
+}
 
 // Query heads per KV head the decode kernels serve together (head slots of
 // their matrix-core tiles).

@@ -114,13 +114,15 @@ __device__ __forceinline__ void load_lds16_sbase(const void* sbase, uint32_t vof
 // Buffer resource over `bytes` bytes from `base` for untyped loads (no
 // stride, no swizzle, 32-bit data format): a load whose offset lies at or
 // beyond `bytes` touches no memory and returns zeros. All fields are
-// wave-uniform.
+// wave-uniform. `base` is a device address below 2^48 (the API rejects
+// others), so its upper word fits the 16-bit address field and leaves the
+// stride and swizzle fields zero.
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
   i32x4 r;
   r[0] = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(a)));
-  r[1] = __builtin_amdgcn_readfirstlane(static_cast<int>((a >> 32) & 0xFFFFu));
+  r[1] = __builtin_amdgcn_readfirstlane(static_cast<int>(a >> 32));
   r[2] = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
   r[3] = 0x00020000;
   return r;

@@ -601,14 +601,19 @@ void fwd16_kernel(const FwdParams a) {
     // block and down through the second.
     const int dt = seg == 0 ? 1 : -1;
     int tcur = nt > 0 ? tile_at(g) : 0;
-    // Contiguous layout: at step j, the K tile copied (that of step j + 2)
-    // starts at k2 and the V tile (of step j + 1) at v1. Every tile of a
-    // segment is whole but the one holding the last key when Nk is not a
-    // multiple of the tile, streamed at step j_rag of the segment (if at all):
-    // its resource covers only the rows up to the last key.
+    // Contiguous layout: at step j, the V tile copied (that of step j + 1)
+    // starts toff bytes after vbase and the K tile (of step j + 2) toff bytes
+    // after kb2, one tile stride past kbase; toff moves by one stride per
+    // step (below 2^32: the API limits a tensor to 2^31 elements; past a
+    // segment's ends it wraps, but those copies cover no bytes). Every tile
+    // of a segment is whole but the one holding the last key when Nk is not
+    // a multiple of the tile, streamed at step j_rag of the segment (if at
+    // all): its resource covers only the rows up to the last key.
     const int64_t dstep = static_cast<int64_t>(dt) * kBC * kv_rs;
-    const uint16_t* k2 = kbase + static_cast<int64_t>(tcur + 2 * dt) * kBC * kv_rs;
-    const uint16_t* v1 = vbase + static_cast<int64_t>(tcur + dt) * kBC * kv_rs;
+    const uint8_t* kb2 = reinterpret_cast<const uint8_t*>(kbase) + dstep * 2;
+    const uint8_t* vb1 = reinterpret_cast<const uint8_t*>(vbase);
+    uint32_t toff = static_cast<uint32_t>(static_cast<int64_t>(tcur + dt) * kBC * kv_rs * 2);
+    const uint32_t dstep_b = static_cast<uint32_t>(dstep * 2);
     const uint32_t full_bytes = TileLoader<D, NW>::rsrc_bytes(kv_rs32, kBC);
     const int t_rag = (Nk % kBC) ? Nk / kBC : -1;
     int j_rag = t_rag < 0 ? -1 : dt > 0 ? t_rag - tcur : tcur - t_rag;
@@ -672,12 +677,11 @@ void fwd16_kernel(const FwdParams a) {
         // a copy the segment does not have gets a resource over no rows
         const uint32_t kb = j + 2 < nt ? (j + 2 == j_rag ? rag_bytes : full_bytes) : 0u;
         const uint32_t vb = j + 1 < nt ? (j + 1 == j_rag ? rag_bytes : full_bytes) : 0u;
-        cp.kt = buffer_rsrc(k2, kb);
-        cp.vt = buffer_rsrc(v1, vb);
+        cp.kt = buffer_rsrc(kb2 + toff, kb);
+        cp.vt = buffer_rsrc(vb1 + toff, vb);
         cp.kl = sbase + P * kSlotBytes;
         cp.vl = sbase + (3 - P) * kSlotBytes;
-        k2 += dstep;
-        v1 += dstep;
+        toff += dstep_b;
       }
       // first key of this step's tile; whether this wave has rows that see
       // the next step's tile

@@ -32,8 +32,10 @@
  *   - Every tensor pointer is a DEVICE pointer owned by the caller; the
  *     library keeps no pointer after the call returns and allocates nothing.
  *   - Tensors are dense and contiguous in the layouts stated per call. The
- *     Q, K, V, O, q and K/V pool pointers must be 16-byte aligned (else
- *     FA_ERR_BAD_ARG); the kernels move them in 16-byte vectors.
+ *     Q, K, V, O, q and K/V pool pointers must be 16-byte aligned device
+ *     addresses below 2^48, the GPU's virtual address space (else
+ *     FA_ERR_BAD_ARG); the kernels move them in 16-byte vectors and address
+ *     K/V through buffer resources, whose base field holds 48 bits.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Work is enqueued asynchronously on it; outputs are valid once the
  *     stream has been synchronised. Apart from the one scratch buffer of

@@ -81,11 +81,13 @@ def test_forward_null_checks():
 
 def test_forward_alignment_check():
     odd = ctypes.c_void_p(0x1008)
+    high = ctypes.c_void_p(1 << 48)   # aligned, but beyond the 48-bit address space
     p = [FAKE] * 5
-    for i in (0, 1, 2, 3):
-        q = list(p)
-        q[i] = odd
-        assert fwd(ptrs=q) == ARG
+    for bad in (odd, high):
+        for i in (0, 1, 2, 3):
+            q = list(p)
+            q[i] = bad
+            assert fwd(ptrs=q) == ARG
 
 
 def dec(B=2, H=8, Hkv=2, d=128, page=16, max_pages=4, num_pages=8, scale=0.1, splits=0,
