@@ -333,10 +333,13 @@ void fwd16_kernel(const FwdParams a) {
   // read from the block table by a scalar load one step before the copy is
   // issued. A page past the sequence's last one is never read (its resource
   // covers no rows); an id outside the pool is replaced by page 0 and marks
-  // the sequence bad (NaN output, agreed over all waves at the end).
+  // the sequence bad (NaN output, agreed over all waves at the end). The
+  // page index (wave-uniform) and the page's byte offset (below 2^32: the API
+  // limits a pool to 2^31 elements) keep this bookkeeping in scalar registers.
   const int32_t* table = PAGED ? a.block_table + static_cast<int64_t>(b) * a.max_pages : nullptr;
   const int last_page = Nk > 0 ? (Nk - 1) / kPageTokens : 0;
-  const int wave_page = PLoader::page_of_wave(wave);
+  const int wave_page = __builtin_amdgcn_readfirstlane(PLoader::page_of_wave(wave));
+  const uint32_t page_bytes = static_cast<uint32_t>(kv_rs32 * kPageTokens * 2);
   bool bad_page = false;
   // The id as loaded (a vector register, the same in every lane); made
   // wave-uniform only where it is used, a step later, so that the load's
@@ -346,13 +349,11 @@ void fwd16_kernel(const FwdParams a) {
   // Buffer resource over the rows of this wave's page of key tile t that
   // hold keys (none past the sequence's last key: those copy as zeros).
   auto page_rsrc = [&](const uint16_t* base, int id, int t) {
-    if (id < 0 || id >= a.num_pages) {
-      bad_page = true;
-      id = 0;
-    }
-    const int first = t * kBC + wave_page * kPageTokens;
-    const int valid = min(max(Nk - first, 0), kPageTokens);
-    return buffer_rsrc(base + static_cast<int64_t>(id) * kv_rs * kPageTokens,
+    const bool ok = static_cast<uint32_t>(id) < static_cast<uint32_t>(a.num_pages);
+    bad_page = bad_page || !ok;
+    const uint32_t pid = ok ? static_cast<uint32_t>(id) : 0u;
+    const int valid = min(max(Nk - (t * kBC + wave_page * kPageTokens), 0), kPageTokens);
+    return buffer_rsrc(reinterpret_cast<const uint8_t*>(base) + pid * page_bytes,
                        valid > 0 ? static_cast<uint32_t>((valid - 1) * kv_rs32 + D) * 2u : 0u);
   };
 
@@ -667,12 +668,12 @@ void fwd16_kernel(const FwdParams a) {
         // resources built from ids loaded one step earlier; a copy the
         // segment does not have gets a resource over no rows
         const int id_k = __builtin_amdgcn_readfirstlane(raw_k);
-        cp.kt = j + 2 < nt ? page_rsrc(kbase, id_k, tile_at(g + 2)) : buffer_rsrc(kbase, 0u);
-        cp.vt = j + 1 < nt ? page_rsrc(vbase, id_v, tile_at(g + 1)) : buffer_rsrc(vbase, 0u);
+        cp.kt = j + 2 < nt ? page_rsrc(kbase, id_k, tcur + 2 * dt) : buffer_rsrc(kbase, 0u);
+        cp.vt = j + 1 < nt ? page_rsrc(vbase, id_v, tcur + dt) : buffer_rsrc(vbase, 0u);
         cp.kl = sbase + P * kSlotBytes;
         cp.vl = sbase + (3 - P) * kSlotBytes;
         id_v = id_k;
-        if (j + 3 < nt) raw_k = fetch_id(tile_at(g + 3));
+        if (j + 3 < nt) raw_k = fetch_id(tcur + 3 * dt);
       } else {
         // a copy the segment does not have gets a resource over no rows
         const uint32_t kb = j + 2 < nt ? (j + 2 == j_rag ? rag_bytes : full_bytes) : 0u;
@@ -685,9 +686,9 @@ void fwd16_kernel(const FwdParams a) {
       }
       // first key of this step's tile; whether this wave has rows that see
       // the next step's tile
-      const int k0 = (PAGED ? tile_at(g) : tcur) * kBC;
-      const bool nx_ok = j + 1 < nt && (PAGED ? tile_at(g + 1) : tcur + dt) * kBC <= wave_last;
-      if constexpr (!PAGED) tcur += dt;
+      const int k0 = tcur * kBC;
+      const bool nx_ok = j + 1 < nt && (tcur + dt) * kBC <= wave_last;
+      tcur += dt;
       constexpr uint32_t kl = 1 - P;   // K slot of step j + 1
       constexpr uint32_t vl = 2 + P;   // V slot of step j
       if (cur_ok) {
