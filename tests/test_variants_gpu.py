@@ -298,6 +298,47 @@ def test_forward_paged_single_query_rows_are_the_decode():
         assert_lse("one-query rows", np64(l), rl)
 
 
+def test_forward_paged_graph_replays_match_eager():
+    """A ragged batch with one-query sequences (two launches: the decode
+    kernel for those rows, then the tiled kernel) recorded into a graph:
+    every replay, with new queries written in between, equals an eager call
+    bit for bit."""
+    q_lens, kv_lens = [1, 300, 1, 1, 700, 1], [4100, 300, 1, 2000, 900, 77]
+    H, Hkv, d = 32, 8, 128
+    ri = inputs.ragged_paged_inputs(q_lens, kv_lens, H, Hkv, d, seed=56)
+    args = [t.to(DEV) for t in (ri.q, ri.qo_indptr, ri.k_pool, ri.v_pool, ri.block_table,
+                                ri.kv_lens)]
+    o = torch.empty(tuple(ri.q.shape), dtype=torch.float32, device=DEV)
+    lse = torch.empty((ri.q.shape[0], H), dtype=torch.float32, device=DEV)
+    say("forward_paged graph: eager warm-up, capture")
+    fa.forward_paged(*args, ri.max_q_len, causal=True, out_dtype=torch.float32, out=o, lse=lse)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fa.forward_paged(*args, ri.max_q_len, causal=True, out_dtype=torch.float32, out=o,
+                         lse=lse)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(57)
+    for it in range(4):
+        qn = torch.from_numpy(rng.standard_normal(tuple(ri.q.shape)).astype(np.float32))
+        args[0].copy_(qn.to(args[0].dtype))
+        torch.cuda.synchronize()
+        say(f"  replay {it}: eager reference, then graph")
+        eo, el = fa.forward_paged(*args, ri.max_q_len, causal=True, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        o.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, eo) and torch.equal(lse, el), f"replay {it} differs from eager"
+    ro, rl = oracle.attention_ragged_paged(args[0].cpu(), ri.qo_indptr, ri.k_pool, ri.v_pool,
+                                           ri.block_table, ri.kv_lens, 1 / math.sqrt(d), True)
+    assert_lowp_acc("forward_paged graph", np64(o), ro)
+    assert_lse("forward_paged graph", np64(lse), rl)
+    del g
+
+
 def test_forward_paged_single_query_contract_violations_give_nan():
     q_lens, kv_lens = [1, 1, 1, 1, 3], [100, 100, 100, 100, 100]
     ri = inputs.ragged_paged_inputs(q_lens, kv_lens, 8, 2, 128, seed=55)
