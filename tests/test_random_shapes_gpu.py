@@ -7,9 +7,13 @@ head dims, query and key lengths that are and are not multiples
 of the 64-key tile or of a wave's 32 rows (including fewer keys than queries,
 fewer than one tile, and none at all), causal or not, 16-bit and fp32 inputs.
 The sizes stay small enough for the oracle to finish in a second or two.
+
+FA_RANDOM_SHAPES_SCALE=k (default 1) draws k times as many shapes from the
+same seeds; the first draws are the default sweep's.
 """
 
 import math
+import os
 
 import numpy as np
 import pytest
@@ -118,9 +122,10 @@ def _draw_paged_decode_heavy(n, seed):
     return cases
 
 
-DENSE = _draw_dense(24, 7321) + _draw_dense_large(10, 7324)
-PAGED = _draw_paged(12, 7322) + _draw_paged_decode_heavy(8, 7325)
-DECODE = _draw_decode(12, 7323)
+SCALE = max(1, int(os.environ.get("FA_RANDOM_SHAPES_SCALE", "1")))
+DENSE = _draw_dense(24 * SCALE, 7321) + _draw_dense_large(10 * SCALE, 7324)
+PAGED = _draw_paged(12 * SCALE, 7322) + _draw_paged_decode_heavy(8 * SCALE, 7325)
+DECODE = _draw_decode(12 * SCALE, 7323)
 
 
 @pytest.mark.parametrize("case", DENSE, ids=[
