@@ -764,9 +764,17 @@ void fwd16_kernel(const FwdParams a) {
       inv = __builtin_nanf("");
       lse_v = __builtin_nanf("");
     }
+    // This lane's query row and head again (dense layout: from an opaque copy
+    // of the lane index; kept from the segment's start they would hold
+    // registers, and spill, through the key loop).
+    int lane_r = lane;
+    if constexpr (!PAGED) __asm__ volatile("" : "+v"(lane_r));
+    const int prow_e = qw0 + (lane_r & 31);
+    const int qrow_e = prow_e / G;
+    const int h_e = hk * G + (prow_e - qrow_e * G);
     if (partial) {   // key split: fp32 partial (o, lse) of this split
-      if (qrow < Nq) {
-        const int64_t pr = ((q_row0 + qrow) * a.H + h) * S + split;
+      if (qrow_e < Nq) {
+        const int64_t pr = ((q_row0 + qrow_e) * a.H + h_e) * S + split;
         float* prow = a.part_o + pr * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
@@ -813,9 +821,9 @@ void fwd16_kernel(const FwdParams a) {
                 reinterpret_cast<u32x4_t*>(static_cast<OutT*>(a.o) + (q_row0 + qrow2) * q_rs +
                                            static_cast<int64_t>(h2) * D + 8 * c));
         }
-      } else if (qrow < Nq) {
-        OutT* orow = static_cast<OutT*>(a.o) + (q_row0 + qrow) * q_rs +
-                     static_cast<int64_t>(h) * D;
+      } else if (qrow_e < Nq) {
+        OutT* orow = static_cast<OutT*>(a.o) + (q_row0 + qrow_e) * q_rs +
+                     static_cast<int64_t>(h_e) * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -825,9 +833,9 @@ void fwd16_kernel(const FwdParams a) {
                    acc[db][4 * gg + 3] * inv);
       }
       // LSE layout: [B, H, Nq] dense; [total_q, H] for ragged queries.
-      const int64_t li = PAGED ? (q_row0 + qrow) * a.H + h
-                               : (static_cast<int64_t>(b) * a.H + h) * Nq + qrow;
-      if (lane < 32 && qrow < Nq) a.lse[li] = lse_v;
+      const int64_t li = PAGED ? (q_row0 + qrow_e) * a.H + h_e
+                               : (static_cast<int64_t>(b) * a.H + h_e) * Nq + qrow_e;
+      if (lane < 32 && qrow_e < Nq) a.lse[li] = lse_v;
     }
   }
 }
