@@ -258,18 +258,19 @@ def test_forward_paged_equals_dense_forward():
 
 
 def test_forward_paged_contract_violations_give_nan():
-    q_lens, kv_lens = [19, 19, 19, 20], [100, 100, 100, 100]
+    q_lens, kv_lens = [19, 19, 19, 20, 19], [100, 100, 100, 100, 100]
     ri = inputs.ragged_paged_inputs(q_lens, kv_lens, 8, 2, 128, seed=53)
     n_pages = ri.k_pool.shape[0]
     ri.block_table[1, 2] = n_pages          # page id outside the pool
     ri.kv_lens[2] = 10_000                  # longer than the block table allows
+    ri.block_table[4, 5] = -7               # negative page id
     say("forward_paged contract violations")
     for causal in (False, True):
-        # the last sequence is longer than max_q_len = 19
+        # sequence 3 is longer than max_q_len = 19
         o, l = gpu_forward_paged(ri, causal, torch.float32, max_q_len=19)
         assert torch.isfinite(o[:19]).all() and torch.isfinite(l[:19]).all()
-        for b in (1, 2, 3):
-            r0, r1 = 19 * b, 19 * b + q_lens[b]
+        for b in (1, 2, 3, 4):
+            r0, r1 = int(ri.qo_indptr[b]), int(ri.qo_indptr[b + 1])
             assert torch.isnan(o[r0:r1]).all() and torch.isnan(l[r0:r1]).all()
 
 
